@@ -1,0 +1,54 @@
+"""Write tests/golden/tiny_bruteforce.json (run from the repository root).
+
+The pages print no worked example, so the stored values are computed here by
+the 50-digit brute-force implementation in ``oracle/bruteforce.py`` (plain
+loops over the definition: per unmasked position, KL of the renormalised top-K
+teacher distribution from the full-vocabulary student distribution at the K
+cached ids, summed; gradients by central differences).  The definition
+follows the agentlenshq.com page "LLMのための効率的な知識蒸留…", sections
+"1. Top-K Logit Cachingによるオフライン蒸留" and "2. Fused Chunked KL Loss".
+This script calls only ``oracle/`` and the seeded tiny cases.
+"""
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+import mpmath  # noqa: E402
+
+from oracle import bruteforce  # noqa: E402
+from oracle_cases import TINY, tiny_problem  # noqa: E402
+
+
+def s(x):
+    return mpmath.nstr(x, 30)
+
+
+def main():
+    out = {"source": "oracle/bruteforce.py at 50 digits; definition per the agentlenshq.com page, "
+                     "sections '1. Top-K Logit Cachingによるオフライン蒸留' and '2. Fused Chunked KL Loss'",
+           "cases": []}
+    for name, n, d, v, k, seed, masked in TINY:
+        H, W, ids, a, mask = tiny_problem(n, d, v, k, seed, masked)
+        L, lses, rls = bruteforce.loss(H.tolist(), W.tolist(), ids.tolist(), a.tolist(),
+                                       None if mask is None else mask.tolist())
+        dH, dW = bruteforce.grad_fd(H.tolist(), W.tolist(), ids.tolist(), a.tolist(),
+                                    None if mask is None else mask.tolist(), g=0.37)
+        out["cases"].append({
+            "name": name, "n": n, "d": d, "v": v, "k": k, "seed": seed, "masked": list(masked),
+            "H": H.tolist(), "W": W.tolist(), "t_ids": ids.tolist(), "t_logits": a.tolist(),
+            "g": 0.37,
+            "loss": s(L), "lse": [s(x) for x in lses], "row_loss": [s(x) for x in rls],
+            "dH": [[s(x) for x in r] for r in dH], "dW": [[s(x) for x in r] for r in dW],
+        })
+    path = os.path.join(ROOT, "tests", "golden", "tiny_bruteforce.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print("wrote", path)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,106 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutation edits one line of ``oracle/kd_oracle.py``'s source text (a
+dropped term, a wrong sign, a wrong index, a transposed operand, an inverted
+mask), loads the edited copy as a separate module, and runs the pins that do
+not depend on the oracle itself: the 50-digit brute-force fixture (values and
+central-difference gradients), the zero-loss construction and the dZ / dW
+sum-to-zero invariants.  Every mutation must fail at least one of them.
+"""
+import json
+import os
+import types
+
+import mpmath
+import numpy as np
+import pytest
+
+import oracle.kd_oracle as kd
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = open(kd.__file__).read()
+
+MUTATIONS = [
+    ("teacher not renormalised", "p = e / e.sum(axis=1, keepdims=True)", "p = e"),
+    ("entropy sign", "np.where(p > 0.0, p * np.log(p), 0.0)", "np.where(p > 0.0, -p * np.log(p), 0.0)"),
+    ("lse drops the max", "return m + np.log(np.exp(z - m[:, None]).sum(axis=1))",
+     "return np.log(np.exp(z - m[:, None]).sum(axis=1))"),
+    ("lse is the max", "return m + np.log(np.exp(z - m[:, None]).sum(axis=1))", "return m"),
+    ("wrong vocab row", "return h_rows @ w.T", "return h_rows @ np.roll(w, 1, axis=0).T"),
+    ("gather sign", "row_loss[b0 + li] = negent - (p * zg_b).sum(axis=1) + s * lse_b[li]",
+     "row_loss[b0 + li] = negent + (p * zg_b).sum(axis=1) + s * lse_b[li]"),
+    ("dropped entropy term", "row_loss[b0 + li] = negent - (p * zg_b).sum(axis=1) + s * lse_b[li]",
+     "row_loss[b0 + li] = - (p * zg_b).sum(axis=1) + s * lse_b[li]"),
+    ("dropped lse term", "row_loss[b0 + li] = negent - (p * zg_b).sum(axis=1) + s * lse_b[li]",
+     "row_loss[b0 + li] = negent - (p * zg_b).sum(axis=1)"),
+    ("gather off by one", "zg_b = np.take_along_axis(z[li], ids, axis=1)",
+     "zg_b = np.take_along_axis(z[li], (ids + 1) % z.shape[1], axis=1)"),
+    ("mask inverted", "return (np.asarray(mask)[rows] != 0).astype(np.float64)",
+     "return (np.asarray(mask)[rows] == 0).astype(np.float64)"),
+    ("scatter sign", "-p.ravel())", "p.ravel())"),
+    ("scatter dropped", "np.add.at(dz, (r_idx", "(lambda *a: None)(dz, (r_idx"),
+    ("softmax not normalised", "dz = s[:, None] * np.exp(z - lse_b[:, None])",
+     "dz = s[:, None] * np.exp(z)"),
+    ("g ignored", "dz *= g", "dz *= 1.0"),
+    ("dH transposed operand", "dH[b0 + live] = dz @ W", "dH[b0 + live] = dz @ W[::-1]"),
+    ("dW wrong rows", "dW += dz.T @ hs", "dW += dz.T @ hs[::-1]"),
+]
+
+
+def _load_mutant(old, new):
+    assert SRC.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("kd_mutant")
+    mod.__file__ = kd.__file__
+    exec(compile(SRC.replace(old, new), kd.__file__ + "<mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+def _golden():
+    with open(os.path.join(HERE, "golden", "tiny_bruteforce.json")) as f:
+        return json.load(f)["cases"]
+
+
+def _f(x):
+    with mpmath.workdps(50):
+        return float(mpmath.mpf(x))
+
+
+def pins(mod):
+    """Run the independent pins against module ``mod``; raise on any failure."""
+    for c in _golden():
+        H, W = np.array(c["H"]), np.array(c["W"])
+        ids, a = np.array(c["t_ids"]), np.array(c["t_logits"])
+        mask = None
+        if c["masked"]:
+            mask = np.ones(c["n"], np.uint8)
+            mask[c["masked"]] = 0
+        f = mod.kd_forward(H, W, ids, a, mask)
+        L = _f(c["loss"])
+        assert abs(f["loss"] - L) <= 1e-12 * abs(L)
+        np.testing.assert_allclose(f["lse"], [_f(x) for x in c["lse"]], rtol=1e-13)
+        b = mod.kd_backward(H, W, ids, a, mask, g=c["g"], want_dz=True)
+        dH = np.array([[_f(x) for x in r] for r in c["dH"]])
+        dW = np.array([[_f(x) for x in r] for r in c["dW"]])
+        assert np.linalg.norm(b["dH"] - dH) <= 1e-10 * np.linalg.norm(dH)
+        assert np.linalg.norm(b["dW"] - dW) <= 1e-10 * np.linalg.norm(dW)
+        np.testing.assert_allclose(b["dZ"].sum(axis=1), 0.0, atol=1e-13)
+    # zero-loss construction
+    v = d = 64
+    rng = np.random.default_rng(7)
+    ids = np.stack([rng.permutation(v)[:5] for _ in range(4)])
+    a = -np.sort(-3.0 * rng.standard_normal((4, 5)), axis=1)
+    H = np.full((4, d), -1e4)
+    for i in range(4):
+        H[i, ids[i]] = a[i]
+    assert abs(mod.kd_forward(H, np.eye(v), ids, a)["loss"]) <= 1e-12
+
+
+def test_unmutated_oracle_passes_pins():
+    pins(_load_mutant("", ""))
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(name, old, new):
+    mod = _load_mutant(old, new)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        pins(mod)
