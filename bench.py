@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused chunked top-K KL loss (forward + backward) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over the workload: kd_chunked_fwd
+(per chunk: teacher renormalisation, fused projection + online logsumexp +
+top-K gather, merge, running-loss fold) then kd_chunked_bwd (per chunk:
+recomputed projection + closed-form dZ, dH = dZ W, dW += dZ^T H).  Inputs are
+seeded synthetic tensors already resident in HBM when timing starts; dW keeps
+accumulating across steps (it is zeroed once, outside the timed region).
+
+Prints ONE JSON line: tokens/s (value), TFLOP/s counted as 8*N*D*V per step
+and its fraction of the bf16 dense matrix-core peak, peak HBM GiB, a roofline
+record of the dominant kernel (per-kernel durations from HIP events recorded
+on the launch stream during the timed steps), and the fp64 CPU oracle timed
+on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2516.6   # dense bf16 matrix cores: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_F32_TFLOPS = 157.3     # dense fp32 matrix cores
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "fused KL fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak); peak GiB"
+GEMM_KINDS = ("fwd_proj", "bwd_dz", "bwd_dh", "bwd_dw")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt-oss-20b-32k")
+    ap.add_argument("--chunk", type=int, default=None, help="override the workload's chunk size")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with rocprofv3 FETCH/WRITE traffic of the dominant kernel")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, rows_n):
+    import numpy as np
+
+    import oracle
+    from chunked_kl_loss_row_amd import inputs
+
+    wl = inp["wl"]
+    rows = inputs.sample_rows(wl.n, rows_n, seed=1)
+    Hs = oracle.widen(inp["H"][rows], wl.x_dtype)
+    Wx = oracle.widen(inp["W"], wl.x_dtype)
+    ids = inp["t_ids"][rows]
+    lg = oracle.widen(inp["t_logits"][rows], wl.t_dtype)
+    m = None if inp["mask"] is None else inp["mask"][rows]
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.kd_forward(Hs, Wx, ids, lg, m)
+    oracle.kd_backward(Hs, Wx, ids, lg, m, want_dw=True)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": rows.size / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows.size} seeded positions of {wl.name} (fp64 numpy dense forward + backward "
+                      f"incl. their dW contribution), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); "
+              f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from chunked_kl_loss_row_amd import binding as B
+    from chunked_kl_loss_row_amd import inputs
+    from chunked_kl_loss_row_amd import loss as L
+
+    torch.cuda.set_device(0)
+    wl = inputs.workload(args.workload)
+    chunk = args.chunk or wl.chunk
+    print(f"[bench] generating {wl.name}: n={wl.n} d={wl.d} v={wl.v} k={wl.k} chunk={chunk}",
+          file=sys.stderr, flush=True)
+    inp = inputs.make_inputs(wl, seed=0)
+
+    import numpy as np
+
+    def dev(a, tag=None):
+        if a is None:
+            return None
+        if tag == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    H, W = dev(inp["H"], wl.x_dtype), dev(inp["W"], wl.x_dtype)
+    ids, lg = dev(inp["t_ids"]), dev(inp["t_logits"], wl.t_dtype)
+    mask = dev(inp["mask"])
+    prob = L.make_problem(H, W, ids, lg, chunk)
+    ws = L.workspace_for(prob, H.device)
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    lse = torch.empty(wl.n, dtype=torch.float32, device="cuda")
+    dH = torch.empty(wl.n, wl.d, dtype=torch.float32, device="cuda")
+    dW = torch.zeros(wl.v, wl.d, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.kd_chunked_fwd(prob, H, W, ids, lg, mask, loss, lse, None, None, ws, stream=stream)
+        B.kd_chunked_bwd(prob, H, W, ids, lg, mask, lse, None, dH, dW, ws, stream=stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    B.kd_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kern = B.kd_profile_all()
+    B.kd_profile_enable(False)
+    peak_gib = torch.cuda.max_memory_allocated() / 2 ** 30
+    loss_v = float(loss.item())
+
+    N, D, V = wl.n, wl.d, wl.v
+    flops_step = 8.0 * N * D * V
+    tflops = flops_step / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.x_dtype == "bf16" else PEAK_F32_TFLOPS
+    kernels = {k: {"avg_ms": (t / n if n else None), "launches_per_step": n / args.steps,
+                   "ms_per_step": t / args.steps} for k, (t, n) in kern.items()}
+    dom = max(kern, key=lambda k: kern[k][0])
+    roofline = None
+    if dom in GEMM_KINDS and kern[dom][1] > 0:
+        per_launch_flop = 2.0 * N * D * V / (kern[dom][1] / args.steps)
+        avg_s = kern[dom][0] / kern[dom][1] * 1e-3
+        ach = per_launch_flop / avg_s / 1e12
+        traffic = None
+        if args.traffic and os.path.exists(args.traffic):
+            with open(args.traffic) as f:
+                tr = json.load(f)
+            if tr.get("kernel") == dom:
+                traffic = tr.get("bytes_per_launch")
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
+                    "algorithmic_flop_per_launch": per_launch_flop, "avg_launch_ms": round(avg_s * 1e3, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu oracle baseline on {args.cpu_rows} rows", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, args.cpu_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": round(N / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.x_dtype,
+        "data": "synthetic (seeded; shapes and value recipe of the workload)",
+        "config": {"workload": wl.name, "n": N, "d": D, "v": V, "k": wl.k, "chunk": chunk,
+                   "mask": wl.mask, "ids": wl.ids, "parallelism": "none (1 GPU)"},
+        "tflops": round(tflops, 2),
+        "pct_peak": round(100.0 * tflops / peak, 2),
+        "peak_gib": round(peak_gib, 3),
+        "loss": loss_v,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,296 @@
+// C ABI of the fused chunked top-K KL loss: argument checks, workspace
+// layout and the chunk scheduler.  See include/kd_chunked.h for the contract.
+//
+// The scheduler walks the rows in contiguous chunks of `chunk` rows (the last
+// one ragged) and enqueues each chunk's kernels on the caller's stream, reusing
+// one workspace whose size depends on the chunk, never on n: memory grows with
+// the sequence only through the caller's own inputs and outputs (aivibenews.ru
+// page "Дистилляция LLM на одной GPU…", section "Два приёма"; agentlenshq.com
+// page "LLMのための効率的な知識蒸留…", section "2. Fused Chunked KL Loss").
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "kd_chunked.h"
+#include "kd_internal.h"
+#include "kd_profile.h"
+
+namespace {
+
+using kd::ChunkArgs;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dtype_ok(int t) { return t == KD_F32 || t == KD_BF16; }
+
+// Workspace regions, as byte offsets from the aligned base.
+struct Layout {
+  int nvt, ldz, split, kslice;
+  size_t keys, psort, zgs, negent, ssum, lb, pm, ps, rl, loss_acc, dz, dhp;
+  size_t total;  // bytes from the aligned base
+};
+
+Layout layout_for(const kd_problem& p) {
+  Layout L{};
+  const size_t C = static_cast<size_t>(p.chunk), K = static_cast<size_t>(p.k);
+  L.nvt = (p.v + kd::kProjBN - 1) / kd::kProjBN;
+  L.ldz = L.nvt * kd::kProjBN;
+  L.split = kd::dh_split_for(p.chunk, p.d, L.ldz, &L.kslice);
+  const size_t xs = p.x_dtype == KD_BF16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&o](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.keys = take(C * K * 4);
+  L.psort = take(C * K * 4);
+  L.zgs = take(C * K * 4);
+  L.negent = take(C * 4);
+  L.ssum = take(C * 4);
+  L.lb = take(C * (static_cast<size_t>(L.nvt) + 1) * 2);
+  L.pm = take(C * L.nvt * 4);
+  L.ps = take(C * L.nvt * 4);
+  L.rl = take(C * 8);
+  L.loss_acc = take(8);
+  L.dz = take(C * static_cast<size_t>(L.ldz) * xs);
+  L.dhp = take(L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
+  L.total = o;
+  return L;
+}
+
+int check_problem(const kd_problem* p) {
+  if (!p) return KD_ERR_NULL;
+  if (p->n < 0 || p->d < 1 || p->v < 1 || p->v > 16777215 || p->k < 1 || p->k > 256 || p->k > p->v ||
+      p->chunk < 1)
+    return KD_ERR_SHAPE;
+  if (!dtype_ok(p->x_dtype) || !dtype_ok(p->t_dtype)) return KD_ERR_DTYPE;
+  if (p->d % 8 != 0) return KD_ERR_ALIGN;
+  return KD_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// 0 = unknown, 1 = gfx950, 2 = other
+std::atomic<int> g_dev_kind[256];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return KD_ERR_DEVICE;
+  int kind = g_dev_kind[dev].load(std::memory_order_relaxed);
+  if (kind == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KD_ERR_DEVICE;
+    kind = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_kind[dev].store(kind, std::memory_order_relaxed);
+  }
+  return kind == 1 ? KD_OK : KD_ERR_DEVICE;
+}
+
+char* ws_base(void* ws) {
+  return reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + kAlign - 1) / kAlign * kAlign);
+}
+
+// ---- optional per-kernel event timing (kd_profile.h) ----
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<ProfRec> g_prof_pending;
+std::vector<hipEvent_t> g_prof_pool;
+double g_prof_ms[KD_K_COUNT];
+int64_t g_prof_n[KD_K_COUNT];
+const char* const g_prof_names[KD_K_COUNT] = {"prep", "fwd_proj", "merge", "loss_fold",
+                                              "bwd_dz", "bwd_dh", "dh_reduce", "bwd_dw"};
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void prof_drain() {  // caller holds g_prof_mu
+  for (const ProfRec& r : g_prof_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      g_prof_ms[r.kind] += ms;
+      g_prof_n[r.kind] += 1;
+    }
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_pending.clear();
+}
+
+// Enqueue `launch` on stream `s`, bracketed by events when profiling is on.
+template <class F>
+void timed(int kind, hipStream_t s, F&& launch) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) {
+    launch();
+    return;
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (a) (void)hipEventRecord(a, s);
+  launch();
+  if (b) (void)hipEventRecord(b, s);
+  if (a && b) g_prof_pending.push_back({kind, a, b});
+}
+
+ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const void* H, const void* W,
+                     const int32_t* ids, const void* logits, const uint8_t* mask, int64_t row0, int rows) {
+  ChunkArgs a{};
+  const size_t xs = p.x_dtype == KD_BF16 ? 2 : 4, ts = p.t_dtype == KD_BF16 ? 2 : 4;
+  a.rows = rows;
+  a.d = p.d;
+  a.v = p.v;
+  a.k = p.k;
+  a.nvt = L.nvt;
+  a.ldz = L.ldz;
+  a.x_bf16 = p.x_dtype == KD_BF16;
+  a.t_bf16 = p.t_dtype == KD_BF16;
+  a.H = static_cast<const char*>(H) + static_cast<size_t>(row0) * p.d * xs;
+  a.W = W;
+  a.ids = ids + row0 * p.k;
+  a.logits = static_cast<const char*>(logits) + static_cast<size_t>(row0) * p.k * ts;
+  a.mask = mask ? mask + row0 : nullptr;
+  a.keys = reinterpret_cast<uint32_t*>(base + L.keys);
+  a.psort = reinterpret_cast<float*>(base + L.psort);
+  a.zgs = reinterpret_cast<float*>(base + L.zgs);
+  a.negent = reinterpret_cast<float*>(base + L.negent);
+  a.ssum = reinterpret_cast<float*>(base + L.ssum);
+  a.lb = reinterpret_cast<uint16_t*>(base + L.lb);
+  a.pm = reinterpret_cast<float*>(base + L.pm);
+  a.ps = reinterpret_cast<float*>(base + L.ps);
+  a.rl = reinterpret_cast<double*>(base + L.rl);
+  a.loss_acc = reinterpret_cast<double*>(base + L.loss_acc);
+  a.dz = base + L.dz;
+  a.dhp = reinterpret_cast<float*>(base + L.dhp);
+  a.dh_split = L.split;
+  a.dh_kslice = L.kslice;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kd_chunked_workspace_size(const kd_problem* prob) {
+  if (check_problem(prob) != KD_OK) return 0;
+  return layout_for(*prob).total + kAlign;  // slack to align the caller's base
+}
+
+const char* kd_status_string(int status) {
+  switch (status) {
+    case KD_OK: return "KD_OK";
+    case KD_ERR_NULL: return "KD_ERR_NULL: a required pointer is NULL";
+    case KD_ERR_SHAPE: return "KD_ERR_SHAPE: invalid problem sizes";
+    case KD_ERR_DTYPE: return "KD_ERR_DTYPE: unsupported dtype";
+    case KD_ERR_ALIGN: return "KD_ERR_ALIGN: d must be a multiple of 8 and tensors 16-byte aligned";
+    case KD_ERR_WORKSPACE: return "KD_ERR_WORKSPACE: workspace too small";
+    case KD_ERR_DEVICE: return "KD_ERR_DEVICE: current device is not a gfx950 GPU";
+    case KD_ERR_LAUNCH: return "KD_ERR_LAUNCH: the HIP runtime reported a launch error";
+    default: return "unknown kd_status";
+  }
+}
+
+int kd_chunked_fwd(const kd_problem* prob, const void* H, const void* W, const int32_t* t_ids,
+                   const void* t_logits, const uint8_t* mask, float* loss, float* lse, float* row_loss,
+                   float* zg, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(prob);
+  if (st != KD_OK) return st;
+  const kd_problem& p = *prob;
+  if (!loss) return KD_ERR_NULL;
+  if (p.n > 0 && (!H || !W || !t_ids || !t_logits || !lse || !workspace)) return KD_ERR_NULL;
+  if (p.n > 0 && (!aligned16(H) || !aligned16(W))) return KD_ERR_ALIGN;
+  if (p.n > 0 && workspace_bytes < kd_chunked_workspace_size(prob)) return KD_ERR_WORKSPACE;
+  st = check_device();
+  if (st != KD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (p.n == 0) {
+    kd::launch_zero_loss(loss, s);
+    return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+  }
+  const Layout L = layout_for(p);
+  char* base = ws_base(workspace);
+  const int64_t nchunks = (p.n + p.chunk - 1) / p.chunk;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t row0 = c * p.chunk;
+    const int rows = static_cast<int>(p.n - row0 < p.chunk ? p.n - row0 : p.chunk);
+    const ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows);
+    timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
+    timed(KD_K_FWD_PROJ, s, [&] { kd::launch_fwd_proj(a, s); });
+    timed(KD_K_MERGE, s, [&] {
+      kd::launch_merge(a, lse + row0, row_loss ? row_loss + row0 : nullptr, zg ? zg + row0 * p.k : nullptr, s);
+    });
+    timed(KD_K_LOSS, s, [&] { kd::launch_loss_fold(a, c == 0, c == nchunks - 1, loss, s); });
+  }
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W, const int32_t* t_ids,
+                   const void* t_logits, const uint8_t* mask, const float* lse, const float* grad_loss,
+                   float* dH, float* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(prob);
+  if (st != KD_OK) return st;
+  const kd_problem& p = *prob;
+  if (p.n > 0 && (!H || !W || !t_ids || !t_logits || !lse || !dH || !dW || !workspace)) return KD_ERR_NULL;
+  if (p.n > 0 && (!aligned16(H) || !aligned16(W) || !aligned16(dH))) return KD_ERR_ALIGN;
+  if (p.n > 0 && workspace_bytes < kd_chunked_workspace_size(prob)) return KD_ERR_WORKSPACE;
+  st = check_device();
+  if (st != KD_OK) return st;
+  if (p.n == 0) return KD_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const Layout L = layout_for(p);
+  char* base = ws_base(workspace);
+  const int64_t nchunks = (p.n + p.chunk - 1) / p.chunk;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t row0 = c * p.chunk;
+    const int rows = static_cast<int>(p.n - row0 < p.chunk ? p.n - row0 : p.chunk);
+    const ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows);
+    timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
+    timed(KD_K_BWD_DZ, s, [&] { kd::launch_bwd_dz(a, lse + row0, grad_loss, s); });
+    timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
+    if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
+    timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
+  }
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+int kd_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_drain();
+  for (int i = 0; i < KD_K_COUNT; ++i) {
+    g_prof_ms[i] = 0.0;
+    g_prof_n[i] = 0;
+  }
+  g_prof_on.store(on != 0, std::memory_order_relaxed);
+  return KD_OK;
+}
+
+int kd_profile_read(int kind, const char** name, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= KD_K_COUNT) return KD_ERR_SHAPE;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_drain();
+  if (name) *name = g_prof_names[kind];
+  if (total_ms) *total_ms = g_prof_ms[kind];
+  if (launches) *launches = g_prof_n[kind];
+  return KD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Internal interface between the C ABI (kd_api.hip) and the kernels
+// (kd_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kd {
+
+// Tile shapes fixed at compile time (they also fix the workspace layout).
+constexpr int kProjBM = 256;   // chunk rows per projection tile
+constexpr int kProjBN = 256;   // vocabulary entries per projection tile
+constexpr int kGradBM = 256;   // output rows per dH / dW tile
+constexpr int kGradBN = 192;   // hidden columns per dH / dW tile
+constexpr int kMaxSplit = 16;  // largest split of the dH reduction over V
+
+// Everything one chunk's kernels need.  Input pointers are already offset
+// to the chunk's first row; workspace pointers are chunk-local.
+struct ChunkArgs {
+  int rows;      // rows in this chunk (<= chunk)
+  int d, v, k;
+  int nvt;       // vocabulary tiles of the projection (ceil(v / kProjBN))
+  int ldz;       // row stride of dZ in elements (nvt * kProjBN)
+  int x_bf16;    // 1: H, W, dZ are bf16; 0: fp32
+  int t_bf16;    // 1: teacher logits are bf16; 0: fp32
+  const void* H;
+  const void* W;
+  const int32_t* ids;
+  const void* logits;
+  const uint8_t* mask;
+  // workspace (chunk-local)
+  uint32_t* keys;   // [chunk][k] teacher (id << 8 | k), ascending
+  float* psort;     // [chunk][k] p in key order
+  float* zgs;       // [chunk][k] gathered student logits in key order
+  float* negent;    // [chunk] sum_k p log p
+  float* ssum;      // [chunk] sum_k p
+  uint16_t* lb;     // [chunk][nvt+1] first key index whose id >= t * kProjBN
+  float* pm;        // [chunk][nvt] per-tile row max of z
+  float* ps;        // [chunk][nvt] per-tile sum of exp(z - max)
+  double* rl;       // [chunk] per-row loss
+  double* loss_acc; // [1] running loss
+  void* dz;         // [chunk][ldz] dZ in x dtype
+  float* dhp;       // [split][chunk][d] split partials of dH
+  int dh_split;     // number of V slices of the dH reduction
+  int dh_kslice;    // V entries per slice (multiple of the k tile)
+};
+
+int dh_split_for(int chunk, int d, int ldz, int* kslice);
+
+void launch_prep(const ChunkArgs& a, hipStream_t s);
+void launch_fwd_proj(const ChunkArgs& a, hipStream_t s);
+void launch_merge(const ChunkArgs& a, float* lse, float* row_loss, float* zg, hipStream_t s);
+void launch_loss_fold(const ChunkArgs& a, int first, int last, float* loss, hipStream_t s);
+void launch_zero_loss(float* loss, hipStream_t s);
+void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);
+void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s);
+void launch_dh_reduce(const ChunkArgs& a, float* dH, hipStream_t s);
+void launch_bwd_dw(const ChunkArgs& a, float* dW, hipStream_t s);
+
+}  // namespace kd

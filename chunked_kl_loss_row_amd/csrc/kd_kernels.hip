@@ -1,0 +1,585 @@
+// Kernels of the fused chunked top-K KL loss (gfx950).
+//
+// Per chunk of rows (the pages' "one chunk of the sequence at a time":
+// agentlenshq.com page "LLMのための効率的な知識蒸留…", section
+// "2. Fused Chunked KL Loss"):
+//   forward : k_prep -> k_fwd_proj -> k_merge -> k_loss_fold
+//   backward: k_prep -> k_bwd_dz -> k_bwd_dh (+ k_dh_reduce) -> k_bwd_dw
+// The per-chunk logit tile lives only in registers / LDS in the forward; in
+// the backward the closed-form dZ of one chunk is written to the workspace
+// (bounded by the chunk size) and consumed by the two gradient GEMMs.
+#include <math.h>
+
+#include "kd_device.h"
+#include "kd_internal.h"
+
+namespace kd {
+
+template <typename T>
+using ProjGemm = Gemm<T, kProjBM, kProjBN, 2, 2, true, true>;
+template <typename T>
+using DhGemm = Gemm<T, kGradBM, kGradBN, 2, 2, true, false>;
+template <typename T>
+using DwGemm = Gemm<T, kGradBM, kGradBN, 2, 2, false, false>;
+
+constexpr int kStageRows = 128;          // rows of the fp32 epilogue stage
+constexpr int kStagePitch = kProjBN + 4; // floats per stage row
+
+// ---------------------------------------------------------------------------
+// teacher record -> renormalised distribution, id-sorted keys, tile ranges
+// ---------------------------------------------------------------------------
+// One wave per row.  p = softmax of the K cached teacher logits (the top-K
+// record renormalised over its entries); negent = sum p log p; s = sum p.
+// keys = (id << 8 | k) sorted ascending with p / zg slots in the same order;
+// lb[t] = index of the first key whose id lies in vocabulary tile >= t, so
+// the keys falling in tile t are [lb[t], lb[t+1]).  Masked rows read
+// nothing and get empty ranges.
+template <typename TT>
+__global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
+                                              const TT* __restrict__ logits,
+                                              const uint8_t* __restrict__ mask, int rows, int K,
+                                              int nvt, uint32_t* __restrict__ keys,
+                                              float* __restrict__ psort, float* __restrict__ zgs,
+                                              float* __restrict__ negent, float* __restrict__ ssum,
+                                              uint16_t* __restrict__ lb) {
+  __shared__ uint32_t s_key[4][256];
+  __shared__ uint32_t s_sorted[4][256];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + w;
+  const bool valid = row < rows;
+  const bool live = valid && (mask == nullptr || mask[row] != 0);
+  const long rbase = static_cast<long>(row) * K;
+
+  uint32_t key[4];
+  float p[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    key[q] = 0xFFFFFFFFu;
+    p[q] = 0.f;
+  }
+  if (live) {
+    float a[4];
+    float amax = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = lane + 64 * q;
+      a[q] = -INFINITY;
+      if (k < K) {
+        key[q] = (static_cast<uint32_t>(ids[rbase + k]) << 8) | static_cast<uint32_t>(k);
+        a[q] = Traits<TT>::to_f32(logits[rbase + k]);
+        amax = fmaxf(amax, a[q]);
+      }
+    }
+    amax = wave_max(amax);
+    float e[4], z = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = lane + 64 * q;
+      e[q] = (k < K) ? expf(a[q] - amax) : 0.f;
+      z += e[q];
+    }
+    z = wave_sum(z);
+    float ne = 0.f, s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      p[q] = e[q] / z;
+      ne += (p[q] > 0.f) ? p[q] * logf(p[q]) : 0.f;
+      s += p[q];
+    }
+    ne = wave_sum(ne);
+    s = wave_sum(s);
+    if (lane == 0) {
+      negent[row] = ne;
+      ssum[row] = s;
+    }
+  } else if (valid && lane == 0) {
+    negent[row] = 0.f;
+    ssum[row] = 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s_key[w][lane + 64 * q] = key[q];
+  __syncthreads();
+  if (live) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = lane + 64 * q;
+      if (k < K) {
+        int rank = 0;
+        for (int j = 0; j < K; ++j) rank += (s_key[w][j] < key[q]) ? 1 : 0;
+        keys[rbase + rank] = key[q];
+        psort[rbase + rank] = p[q];
+        zgs[rbase + k] = 0.f;
+        s_sorted[w][rank] = key[q];
+      }
+    }
+  }
+  __syncthreads();
+  if (valid) {
+    uint16_t* lbr = lb + static_cast<long>(row) * (nvt + 1);
+    if (!live) {
+      for (int t = lane; t <= nvt; t += 64) lbr[t] = 0;
+    } else {
+      for (int j = lane; j < K; j += 64) {
+        const int vt = min(nvt, static_cast<int>((s_sorted[w][j] >> 8) / kProjBN));
+        const int vprev = (j == 0) ? -1 : min(nvt, static_cast<int>((s_sorted[w][j - 1] >> 8) / kProjBN));
+        for (int t = vprev + 1; t <= vt; ++t) lbr[t] = static_cast<uint16_t>(j);
+        if (j == K - 1)
+          for (int t = vt + 1; t <= nvt; ++t) lbr[t] = static_cast<uint16_t>(K);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// helpers shared by the two projection epilogues
+// ---------------------------------------------------------------------------
+// Write the accumulators of the rows in stage half `h` to the fp32 stage.
+template <typename G>
+__device__ __forceinline__ void stage_half(float* stage, const f32x4 (&acc)[G::FM][G::FN], int h) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / 2, wn = wave % 2;
+#pragma unroll
+  for (int fm = 0; fm < G::FM; ++fm) {
+    const int rb = wm * G::WM + fm * 16;
+    if (rb / kStageRows != h) continue;
+#pragma unroll
+    for (int fn = 0; fn < G::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        stage[(rb - h * kStageRows + 4 * (lane >> 4) + r) * kStagePitch + wn * G::WN + fn * 16 +
+              (lane & 15)] = acc[fm][fn][r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// forward: projection + per-tile online (max, sum exp) + top-K gather
+// ---------------------------------------------------------------------------
+// Tile (rt, vt): z = H[rt rows] W[vt vocab]^T on matrix cores.  The epilogue
+// stages z (fp32) in LDS, reduces each row to the tile's max and sum of
+// exp(z - max) and copies z at the row's teacher ids that fall in the tile
+// (the gather is a copy of the accumulator, bit for bit).  Logits never reach
+// HBM.
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_fwd_proj(const T* __restrict__ H, const T* __restrict__ W,
+                                                     int rows, int d, int v, int nvt, int K,
+                                                     const uint16_t* __restrict__ lb,
+                                                     const uint32_t* __restrict__ keys,
+                                                     float* __restrict__ zgs, float* __restrict__ pm,
+                                                     float* __restrict__ ps) {
+  using G = ProjGemm<T>;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  __shared__ int s_lo[G::BM], s_hi[G::BM];
+  const int rtn = (rows + G::BM - 1) / G::BM;
+  const int t = xcd_tile(blockIdx.x, rtn * nvt);
+  if (t < 0) return;
+  const int vt = t / rtn, rt = t % rtn;
+  const int tid = threadIdx.x;
+  for (int r = tid; r < G::BM; r += G::NT) {
+    const int gr = rt * G::BM + r;
+    int lo = 0, hi = 0;
+    if (gr < rows) {
+      lo = lb[static_cast<long>(gr) * (nvt + 1) + vt];
+      hi = lb[static_cast<long>(gr) * (nvt + 1) + vt + 1];
+    }
+    s_lo[r] = lo;
+    s_hi[r] = hi;
+  }
+  f32x4 acc[G::FM][G::FN];
+  G::run(H, d, rt * G::BM, rows, d, W, d, vt * G::BN, v, d, 0, d, reinterpret_cast<T*>(smem), acc);
+
+  float* stage = reinterpret_cast<float*>(smem);
+  const int ncols = min(G::BN, v - vt * G::BN);
+  const int g16 = tid >> 4, l16 = tid & 15;
+#pragma unroll
+  for (int h = 0; h < G::BM / kStageRows; ++h) {
+    stage_half<G>(stage, acc, h);
+    __syncthreads();
+    for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
+      const int row = h * kStageRows + rr, grow = rt * G::BM + row;
+      if (grow >= rows) break;
+      f32x4 x[G::BN / 64];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < G::BN / 64; ++j) {
+        const int c0 = j * 64 + l16 * 4;
+        x[j] = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + c0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c0 + e < ncols) mx = fmaxf(mx, x[j][e]);
+      }
+      mx = group16_max(mx);
+      float sm = 0.f;
+#pragma unroll
+      for (int j = 0; j < G::BN / 64; ++j) {
+        const int c0 = j * 64 + l16 * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c0 + e < ncols) sm += fast_exp2((x[j][e] - mx) * kLog2e);
+      }
+      sm = group16_sum(sm);
+      if (l16 == 0) {
+        pm[static_cast<long>(grow) * nvt + vt] = mx;
+        ps[static_cast<long>(grow) * nvt + vt] = sm;
+      }
+      const int lo = s_lo[row], hi = s_hi[row];
+      for (int j = lo + l16; j < hi; j += 16) {
+        const int col = static_cast<int>(keys[static_cast<long>(grow) * K + j] >> 8) - vt * G::BN;
+        zgs[static_cast<long>(grow) * K + j] = stage[rr * kStagePitch + col];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// forward: merge tile partials -> lse, row loss, gathered logits
+// ---------------------------------------------------------------------------
+// lse_i = M + log sum_t s_t exp(m_t - M) over the vocabulary tiles (fixed
+// order).  row_loss_i = m_i (negent_i - sum_k p_ik zg_ik + s_i lse_i), the
+// KL of the renormalised teacher from the student at the K ids.
+__global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm, const float* __restrict__ ps,
+                                               int nvt, const uint32_t* __restrict__ keys,
+                                               const float* __restrict__ psort,
+                                               const float* __restrict__ zgs,
+                                               const float* __restrict__ negent,
+                                               const float* __restrict__ ssum,
+                                               const uint8_t* __restrict__ mask, int rows, int K,
+                                               float* __restrict__ lse_out, float* __restrict__ rl_out,
+                                               float* __restrict__ zg_out, double* __restrict__ rl_ws) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + w;
+  if (row >= rows) return;
+  const long pb = static_cast<long>(row) * nvt;
+  float M = -INFINITY;
+  for (int t = lane; t < nvt; t += 64) M = fmaxf(M, pm[pb + t]);
+  M = wave_max(M);
+  float S = 0.f;
+  for (int t = lane; t < nvt; t += 64) S += ps[pb + t] * fast_exp2((pm[pb + t] - M) * kLog2e);
+  S = wave_sum(S);
+  const double lse = static_cast<double>(M) + log(static_cast<double>(S));
+  const bool live = (mask == nullptr || mask[row] != 0);
+  const long kb = static_cast<long>(row) * K;
+  double dot = 0.0;
+  if (live)
+    for (int j = lane; j < K; j += 64) dot += static_cast<double>(psort[kb + j]) * static_cast<double>(zgs[kb + j]);
+  dot = wave_sum(dot);
+  const double rl = live ? static_cast<double>(negent[row]) - dot + static_cast<double>(ssum[row]) * lse : 0.0;
+  if (lane == 0) {
+    lse_out[row] = static_cast<float>(lse);
+    rl_ws[row] = rl;
+    if (rl_out) rl_out[row] = static_cast<float>(rl);
+  }
+  if (zg_out) {
+    for (int j = lane; j < K; j += 64) {
+      if (live)
+        zg_out[kb + (keys[kb + j] & 0xFFu)] = zgs[kb + j];
+      else
+        zg_out[kb + j] = 0.f;
+    }
+  }
+}
+
+// Running loss: the chunk's row losses summed in a fixed order (fp64) and
+// folded into the accumulator; the last chunk writes the fp32 loss.
+__global__ __launch_bounds__(256) void k_loss_fold(const double* __restrict__ rl, int rows,
+                                                   double* __restrict__ acc, int first, int last,
+                                                   float* __restrict__ loss) {
+  __shared__ double s[256];
+  double x = 0.0;
+  for (int i = threadIdx.x; i < rows; i += 256) x += rl[i];
+  s[threadIdx.x] = x;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double a = (first ? 0.0 : acc[0]) + s[0];
+    acc[0] = a;
+    if (last) loss[0] = static_cast<float>(a);
+  }
+}
+
+__global__ void k_zero_loss(float* loss) { loss[0] = 0.f; }
+
+// ---------------------------------------------------------------------------
+// backward: recompute the projection and form the closed-form dZ
+// ---------------------------------------------------------------------------
+// dZ_iv = g m_i (s_i exp(z_iv - lse_i) - sum_k p_ik [t_ik = v]), evaluated in
+// fp32 with the -p terms applied before the single rounding to the storage
+// dtype.  Columns in [v, ldz) are written as zeros (padding of the row).
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_bwd_dz(const T* __restrict__ H, const T* __restrict__ W,
+                                                   int rows, int d, int v, int nvt, int K, int ldz,
+                                                   const uint16_t* __restrict__ lb,
+                                                   const uint32_t* __restrict__ keys,
+                                                   const float* __restrict__ psort,
+                                                   const float* __restrict__ ssum,
+                                                   const uint8_t* __restrict__ mask,
+                                                   const float* __restrict__ lse,
+                                                   const float* __restrict__ gptr, T* __restrict__ dz) {
+  using G = ProjGemm<T>;
+  using Tr = Traits<T>;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  __shared__ int s_lo[G::BM], s_hi[G::BM];
+  __shared__ float s_lse2[G::BM], s_coef[G::BM], s_gm[G::BM];
+  __shared__ int s_live[G::BM];
+  const int rtn = (rows + G::BM - 1) / G::BM;
+  const int t = xcd_tile(blockIdx.x, rtn * nvt);
+  if (t < 0) return;
+  const int vt = t / rtn, rt = t % rtn;
+  const int tid = threadIdx.x;
+  const float g = gptr ? gptr[0] : 1.f;
+  for (int r = tid; r < G::BM; r += G::NT) {
+    const int gr = rt * G::BM + r;
+    int lo = 0, hi = 0;
+    float lse2 = 0.f, coef = 0.f, gm = 0.f;
+    int live = 0;
+    if (gr < rows) {
+      live = (mask == nullptr || mask[gr] != 0) ? 1 : 0;
+      lse2 = lse[gr] * kLog2e;
+      if (live) {
+        lo = lb[static_cast<long>(gr) * (nvt + 1) + vt];
+        hi = lb[static_cast<long>(gr) * (nvt + 1) + vt + 1];
+        gm = g;
+        coef = g * ssum[gr];
+      }
+    }
+    s_lo[r] = lo;
+    s_hi[r] = hi;
+    s_lse2[r] = lse2;
+    s_coef[r] = coef;
+    s_gm[r] = gm;
+    s_live[r] = live;
+  }
+  f32x4 acc[G::FM][G::FN];
+  G::run(H, d, rt * G::BM, rows, d, W, d, vt * G::BN, v, d, 0, d, reinterpret_cast<T*>(smem), acc);
+
+  float* stage = reinterpret_cast<float*>(smem);
+  const int g16 = tid >> 4, l16 = tid & 15;
+#pragma unroll
+  for (int h = 0; h < G::BM / kStageRows; ++h) {
+    stage_half<G>(stage, acc, h);
+    __syncthreads();
+    for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
+      const int row = h * kStageRows + rr, grow = rt * G::BM + row;
+      if (grow >= rows) break;
+      const float lse2 = s_lse2[row], coef = s_coef[row], gm = s_gm[row];
+      const int lo = s_lo[row], hi = s_hi[row];
+      const bool live = s_live[row] != 0;
+      T* out = dz + static_cast<long>(grow) * ldz + vt * G::BN;
+#pragma unroll
+      for (int j = 0; j < G::BN / 64; ++j) {
+        const int c0 = j * 64 + l16 * 4;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + c0);
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = live ? coef * fast_exp2(fmaf(x[e], kLog2e, -lse2)) : 0.f;
+        for (int q = lo; q < hi; ++q) {
+          const long kq = static_cast<long>(grow) * K + q;
+          const int c = static_cast<int>(keys[kq] >> 8) - vt * G::BN - c0;
+          if (static_cast<unsigned>(c) < 4u) {
+            const float sub = gm * psort[kq];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c == e) o[e] -= sub;
+          }
+        }
+        const int gc = vt * G::BN + c0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gc + e >= v) o[e] = 0.f;
+        if constexpr (sizeof(T) == 2) {
+          uint32_t lo2 = static_cast<uint32_t>(Tr::from_f32(o[0])) | (static_cast<uint32_t>(Tr::from_f32(o[1])) << 16);
+          uint32_t hi2 = static_cast<uint32_t>(Tr::from_f32(o[2])) | (static_cast<uint32_t>(Tr::from_f32(o[3])) << 16);
+          *reinterpret_cast<uint2*>(out + c0) = make_uint2(lo2, hi2);
+        } else {
+          *reinterpret_cast<f32x4*>(out + c0) = f32x4{o[0], o[1], o[2], o[3]};
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward: dH = dZ W (split over V, fixed-order reduce) and dW += dZ^T H
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_bwd_dh(const T* __restrict__ dz, int ldz,
+                                                   const T* __restrict__ W, int rows, int d, int v,
+                                                   int split, int kslice, float* __restrict__ out,
+                                                   long split_stride) {
+  using G = DhGemm<T>;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  const int mtn = (rows + G::BM - 1) / G::BM, ntn = (d + G::BN - 1) / G::BN;
+  const int t = xcd_tile(blockIdx.x, mtn * ntn * split);
+  if (t < 0) return;
+  const int ks = t / (mtn * ntn), rem = t % (mtn * ntn);
+  const int mt = rem / ntn, nt = rem % ntn;
+  const int k0 = ks * kslice, k1 = min(ldz, k0 + kslice);
+  f32x4 acc[G::FM][G::FN];
+  G::run(dz, ldz, mt * G::BM, rows, ldz, W, d, nt * G::BN, d, v, k0, k1, reinterpret_cast<T*>(smem), acc);
+  float* o = out + ks * split_stride;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / 2, wn = wave % 2;
+#pragma unroll
+  for (int fm = 0; fm < G::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < G::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mt * G::BM + wm * G::WM + fm * 16 + 4 * (lane >> 4) + r;
+        const int col = nt * G::BN + wn * G::WN + fn * 16 + (lane & 15);
+        if (row < rows && col < d) o[static_cast<long>(row) * d + col] = acc[fm][fn][r];
+      }
+}
+
+__global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ part, int split,
+                                                   long split_stride, long count,
+                                                   float* __restrict__ dH) {
+  const long i4 = (static_cast<long>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i4 >= count) return;
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + i4);
+  for (int k = 1; k < split; ++k) s += *reinterpret_cast<const f32x4*>(part + k * split_stride + i4);
+  *reinterpret_cast<f32x4*>(dH + i4) = s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_bwd_dw(const T* __restrict__ dz, int ldz,
+                                                   const T* __restrict__ Hc, int rows, int d, int v,
+                                                   float* __restrict__ dW) {
+  using G = DwGemm<T>;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  const int mtn = (v + G::BM - 1) / G::BM, ntn = (d + G::BN - 1) / G::BN;
+  const int t = xcd_tile(blockIdx.x, mtn * ntn);
+  if (t < 0) return;
+  const int mt = t / ntn, nt = t % ntn;
+  f32x4 acc[G::FM][G::FN];
+  // A(m = vocab, k = chunk row) = dZ[k][m];  B(n = hidden, k = chunk row) = H[k][n]
+  G::run(dz, ldz, mt * G::BM, ldz, rows, Hc, d, nt * G::BN, d, rows, 0, rows,
+         reinterpret_cast<T*>(smem), acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / 2, wn = wave % 2;
+#pragma unroll
+  for (int fm = 0; fm < G::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < G::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mt * G::BM + wm * G::WM + fm * 16 + 4 * (lane >> 4) + r;
+        const int col = nt * G::BN + wn * G::WN + fn * 16 + (lane & 15);
+        if (row < v && col < d) {
+          float* p = dW + static_cast<long>(row) * d + col;
+          *p = *p + acc[fm][fn][r];
+        }
+      }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+int dh_split_for(int chunk, int d, int ldz, int* kslice) {
+  // Split the V reduction so the grid fills the 256 compute units with
+  // little tail: the smallest split whose last wave of workgroups is >= 90%
+  // full, at least 8 k tiles per slice.
+  const int mt = (chunk + kGradBM - 1) / kGradBM, nt = (d + kGradBN - 1) / kGradBN;
+  const int tiles = mt * nt;
+  const int bk = 64;  // k tile of the bf16 engine (the fp32 engine's 32 divides it)
+  int best = 1;
+  for (int s = 1; s <= kMaxSplit; ++s) {
+    if (static_cast<long>(ldz) / s < 8L * bk) break;
+    const long wg = static_cast<long>(tiles) * s;
+    const long full = (wg + 255) / 256 * 256;
+    best = s;
+    if (wg >= 200 && wg * 10 >= full * 9) break;
+  }
+  int ks = (ldz + best - 1) / best;
+  ks = (ks + bk - 1) / bk * bk;
+  *kslice = ks;
+  return (ldz + ks - 1) / ks;
+}
+
+void launch_prep(const ChunkArgs& a, hipStream_t s) {
+  const dim3 grid((a.rows + 3) / 4), block(256);
+  if (a.t_bf16)
+    k_prep<uint16_t><<<grid, block, 0, s>>>(a.ids, static_cast<const uint16_t*>(a.logits), a.mask, a.rows,
+                                            a.k, a.nvt, a.keys, a.psort, a.zgs, a.negent, a.ssum, a.lb);
+  else
+    k_prep<float><<<grid, block, 0, s>>>(a.ids, static_cast<const float*>(a.logits), a.mask, a.rows, a.k,
+                                         a.nvt, a.keys, a.psort, a.zgs, a.negent, a.ssum, a.lb);
+}
+
+void launch_fwd_proj(const ChunkArgs& a, hipStream_t s) {
+  const int rtn = (a.rows + kProjBM - 1) / kProjBM;
+  const dim3 grid(xcd_grid(rtn * a.nvt)), block(256);
+  if (a.x_bf16)
+    k_fwd_proj<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
+                                                static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v,
+                                                a.nvt, a.k, a.lb, a.keys, a.zgs, a.pm, a.ps);
+  else
+    k_fwd_proj<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
+                                             a.rows, a.d, a.v, a.nvt, a.k, a.lb, a.keys, a.zgs, a.pm,
+                                             a.ps);
+}
+
+void launch_merge(const ChunkArgs& a, float* lse, float* row_loss, float* zg, hipStream_t s) {
+  k_merge<<<dim3((a.rows + 3) / 4), dim3(256), 0, s>>>(a.pm, a.ps, a.nvt, a.keys, a.psort, a.zgs, a.negent,
+                                                      a.ssum, a.mask, a.rows, a.k, lse, row_loss, zg,
+                                                      a.rl);
+}
+
+void launch_loss_fold(const ChunkArgs& a, int first, int last, float* loss, hipStream_t s) {
+  k_loss_fold<<<dim3(1), dim3(256), 0, s>>>(a.rl, a.rows, a.loss_acc, first, last, loss);
+}
+
+void launch_zero_loss(float* loss, hipStream_t s) { k_zero_loss<<<dim3(1), dim3(1), 0, s>>>(loss); }
+
+void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s) {
+  const int rtn = (a.rows + kProjBM - 1) / kProjBM;
+  const dim3 grid(xcd_grid(rtn * a.nvt)), block(256);
+  if (a.x_bf16)
+    k_bwd_dz<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
+                                              static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
+                                              a.k, a.ldz, a.lb, a.keys, a.psort, a.ssum, a.mask, lse, g,
+                                              static_cast<uint16_t*>(a.dz));
+  else
+    k_bwd_dz<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
+                                           a.rows, a.d, a.v, a.nvt, a.k, a.ldz, a.lb, a.keys, a.psort,
+                                           a.ssum, a.mask, lse, g, static_cast<float*>(a.dz));
+}
+
+void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s) {
+  const int mtn = (a.rows + kGradBM - 1) / kGradBM, ntn = (a.d + kGradBN - 1) / kGradBN;
+  const int split = a.dh_split;
+  const dim3 grid(xcd_grid(mtn * ntn * split)), block(256);
+  float* out = split == 1 ? dH : a.dhp;
+  const long stride = static_cast<long>(a.rows) * a.d;
+  if (a.x_bf16)
+    k_bwd_dh<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.dz), a.ldz,
+                                              static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, split,
+                                              a.dh_kslice, out, stride);
+  else
+    k_bwd_dh<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.dz), a.ldz,
+                                           static_cast<const float*>(a.W), a.rows, a.d, a.v, split,
+                                           a.dh_kslice, out, stride);
+}
+
+void launch_dh_reduce(const ChunkArgs& a, float* dH, hipStream_t s) {
+  if (a.dh_split <= 1) return;
+  const long count = static_cast<long>(a.rows) * a.d;  // d % 8 == 0, so count % 4 == 0
+  const long nthreads = count / 4;
+  k_dh_reduce<<<dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256), 0, s>>>(a.dhp, a.dh_split, count,
+                                                                                       count, dH);
+}
+
+void launch_bwd_dw(const ChunkArgs& a, float* dW, hipStream_t s) {
+  const int mtn = (a.v + kGradBM - 1) / kGradBM, ntn = (a.d + kGradBN - 1) / kGradBN;
+  const dim3 grid(xcd_grid(mtn * ntn)), block(256);
+  if (a.x_bf16)
+    k_bwd_dw<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.dz), a.ldz,
+                                              static_cast<const uint16_t*>(a.H), a.rows, a.d, a.v, dW);
+  else
+    k_bwd_dw<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.dz), a.ldz,
+                                           static_cast<const float*>(a.H), a.rows, a.d, a.v, dW);
+}
+
+}  // namespace kd

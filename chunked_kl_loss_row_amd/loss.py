@@ -1,0 +1,114 @@
+"""torch-facing wrapper of the fused chunked top-K KL loss.
+
+PyTorch supplies device memory, the current stream and autograd plumbing;
+every arithmetic step runs in libkdchunk.so through ``binding``.
+
+    loss = kd_chunked_kl(hidden, weight, t_ids, t_logits, mask=None, chunk=2048)
+    loss.backward()      # hidden.grad (fp32), weight.grad (fp32 accumulator)
+
+The loss is the sum over unmasked positions of KL(teacher top-K, renormalised
+|| student softmax over the full vocabulary) at the K cached ids; the
+projection ``hidden @ weight.T`` is fused into it and computed one chunk of
+positions at a time, recomputed in the backward pass (agentlenshq.com page
+"LLMのための効率的な知識蒸留…", section "2. Fused Chunked KL Loss").
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+
+def _xdtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return B.KD_BF16
+    if t.dtype == torch.float32:
+        return B.KD_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def make_problem(hidden, weight, t_ids, t_logits, chunk: int) -> B.KDProblem:
+    n, d = hidden.shape
+    v, d2 = weight.shape
+    if d2 != d:
+        raise ValueError("hidden and weight disagree on the hidden size")
+    if t_ids.shape != t_logits.shape or t_ids.shape[0] != n:
+        raise ValueError("teacher ids / logits must be [n, k]")
+    if hidden.dtype != weight.dtype:
+        raise TypeError("hidden and weight must share a dtype")
+    if t_ids.dtype != torch.int32:
+        raise TypeError("teacher ids must be int32")
+    return B.problem(n, d, v, t_ids.shape[1], chunk, _xdtype(hidden), _xdtype(t_logits))
+
+
+def _check(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def workspace_for(prob: B.KDProblem, device) -> torch.Tensor:
+    return torch.empty(B.kd_chunked_workspace_size(prob), dtype=torch.uint8, device=device)
+
+
+def forward(hidden, weight, t_ids, t_logits, mask=None, chunk: int = 2048, workspace=None,
+            row_loss: bool = False, zg: bool = False) -> dict:
+    """Run kd_chunked_fwd; returns {"loss", "lse", "row_loss"?, "zg"?, "workspace"}."""
+    _check(hidden, weight, t_ids, t_logits, mask)
+    prob = make_problem(hidden, weight, t_ids, t_logits, chunk)
+    dev = hidden.device
+    ws = workspace if workspace is not None else workspace_for(prob, dev)
+    out = {"loss": torch.empty(1, dtype=torch.float32, device=dev),
+           "lse": torch.empty(prob.n, dtype=torch.float32, device=dev),
+           "row_loss": torch.empty(prob.n, dtype=torch.float32, device=dev) if row_loss else None,
+           "zg": torch.empty(prob.n, prob.k, dtype=torch.float32, device=dev) if zg else None,
+           "workspace": ws}
+    B.kd_chunked_fwd(prob, hidden, weight, t_ids, t_logits, mask, out["loss"], out["lse"],
+                     out["row_loss"], out["zg"], ws)
+    return out
+
+
+def backward(hidden, weight, t_ids, t_logits, mask, lse, grad_loss=None, dW=None, chunk: int = 2048,
+             workspace=None, dH=None):
+    """Run kd_chunked_bwd; returns (dH, dW).  ``dW`` (fp32) is accumulated
+    into when given, else a zero buffer is made."""
+    _check(hidden, weight, t_ids, t_logits, mask, lse, grad_loss)
+    prob = make_problem(hidden, weight, t_ids, t_logits, chunk)
+    dev = hidden.device
+    ws = workspace if workspace is not None else workspace_for(prob, dev)
+    if dH is None:
+        dH = torch.empty(prob.n, prob.d, dtype=torch.float32, device=dev)
+    if dW is None:
+        dW = torch.zeros(prob.v, prob.d, dtype=torch.float32, device=dev)
+    if dW.dtype != torch.float32 or dH.dtype != torch.float32:
+        raise TypeError("gradients are fp32")
+    B.kd_chunked_bwd(prob, hidden, weight, t_ids, t_logits, mask, lse, grad_loss, dH, dW, ws)
+    return dH, dW
+
+
+class KDChunkedKL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, hidden, weight, t_ids, t_logits, mask, chunk):
+        out = forward(hidden, weight, t_ids, t_logits, mask, chunk)
+        ctx.save_for_backward(hidden, weight, t_ids, t_logits, mask, out["lse"])
+        ctx.chunk = chunk
+        ctx.workspace = out["workspace"]
+        return out["loss"][0]
+
+    @staticmethod
+    def backward(ctx, g):
+        hidden, weight, t_ids, t_logits, mask, lse = ctx.saved_tensors
+        gl = g.reshape(1).to(torch.float32).contiguous()
+        dH, dW = backward(hidden, weight, t_ids, t_logits, mask, lse, gl, chunk=ctx.chunk,
+                          workspace=ctx.workspace)
+        ctx.workspace = None
+        gh = dH if hidden.dtype == torch.float32 else dH.to(hidden.dtype)
+        gw = dW if weight.dtype == torch.float32 else dW.to(weight.dtype)
+        return gh, gw, None, None, None, None
+
+
+def kd_chunked_kl(hidden, weight, t_ids, t_logits, mask=None, chunk: int = 2048):
+    """0-d fp32 loss; differentiable w.r.t. ``hidden`` and ``weight``."""
+    return KDChunkedKL.apply(hidden, weight, t_ids, t_logits, mask, chunk)

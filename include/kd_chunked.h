@@ -1,0 +1,127 @@
+/*
+ * kd_chunked.h -- C ABI of the fused chunked top-K KL distillation loss
+ * (libkdchunk.so, AMD MI355X / gfx950).
+ *
+ * The operation.  A student projects hidden states H [n,d] through its output
+ * projection W [v,d] to logits z_i = W h_i over the full vocabulary; a cached
+ * teacher record gives, per position, K token ids and K teacher logits.  The
+ * loss is, summed over unmasked positions,
+ *
+ *     L = sum_i m_i sum_k p_ik (log p_ik - z_{i,t_ik} + lse_i),
+ *     p_i = softmax over the K cached teacher logits, lse_i = log sum_v e^{z_iv}
+ *
+ * i.e. KL(teacher || student) on the K cached ids (reading of the pages: the
+ * teacher record is renormalised over its K entries, temperature 1, sum
+ * reduction).  Sources: the offline top-100 teacher cache (agentlenshq.com
+ * page "LLMのための効率的な知識蒸留…", section "1. Top-K Logit Cachingによる
+ * オフライン蒸留"); the fused chunked loss that owns the output projection,
+ * projects one chunk of positions at a time, folds it into a running loss and
+ * discards it, and recomputes each chunk in the backward pass (same page,
+ * section "2. Fused Chunked KL Loss"; aivibenews.ru page "Дистилляция LLM на
+ * одной GPU…", section "Два приёма"); the closed-form gradient the aihot.vn
+ * page "Tối ưu hóa chi phí chưng cất tri thức…" mentions in section "Mô hình
+ * học sinh thu được":  dL/dz_iv = m_i (s_i q_iv - sum_k p_ik [t_ik = v]),
+ * s_i = sum_k p_ik, q_i = softmax(z_i).
+ *
+ * Conventions for every entry point:
+ *  - all tensor pointers are DEVICE pointers on the current HIP device, dense
+ *    row-major, and 16-byte aligned;
+ *  - the caller owns and allocates every buffer, including the workspace
+ *    (size from kd_chunked_workspace_size); the library allocates nothing,
+ *    never synchronises, and only enqueues work on `stream` (a hipStream_t,
+ *    NULL = the null stream).  Calls are asynchronous with respect to the host;
+ *  - one workspace must not be used by two calls in flight at once;
+ *  - arguments are checked on the host before anything is enqueued; on any
+ *    error the call returns a non-zero kd_status and enqueues nothing;
+ *  - no exception crosses the ABI.
+ * Preconditions that are NOT checked: on unmasked rows the ids lie in [0,v)
+ * (ids outside it are never matched; memory stays safe but the result is
+ * meaningless); the backward gets the same inputs as the forward that
+ * produced `lse`.  Repeated ids within a row are handled term by term.
+ * Non-finite inputs propagate to the outputs; no error is raised.
+ */
+#ifndef KD_CHUNKED_H
+#define KD_CHUNKED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kd_status {
+  KD_OK = 0,
+  KD_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  KD_ERR_SHAPE = 2,     /* n < 0, d < 1, v < 1, k not in [1, min(v,256)],
+                           chunk < 1, v > 16777215                              */
+  KD_ERR_DTYPE = 3,     /* x_dtype / t_dtype not a kd_dtype                     */
+  KD_ERR_ALIGN = 4,     /* d % 8 != 0, or a pointer not 16-byte aligned         */
+  KD_ERR_WORKSPACE = 5, /* workspace_bytes < kd_chunked_workspace_size(prob)    */
+  KD_ERR_DEVICE = 6,    /* the current device is not a gfx950                   */
+  KD_ERR_LAUNCH = 7     /* the HIP runtime reported an error while enqueueing  */
+} kd_status;
+
+typedef enum kd_dtype { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
+
+typedef struct kd_problem {
+  int64_t n;       /* positions (batch*seq flattened), >= 0                     */
+  int32_t d;       /* hidden size, multiple of 8                                 */
+  int32_t v;       /* vocabulary size                                            */
+  int32_t k;       /* teacher top-K, 1 <= k <= min(v, 256)                       */
+  int32_t chunk;   /* rows per chunk (the only tuning knob), >= 1               */
+  int32_t x_dtype; /* kd_dtype of H and W (the projection's compute dtype)      */
+  int32_t t_dtype; /* kd_dtype of the teacher logits                            */
+} kd_problem;
+
+/* Bytes of workspace the fwd and bwd calls need for `prob`.  Depends on
+ * (d, v, k, chunk, dtypes) only, never on n: the per-chunk logit grid lives
+ * in it, the N x V grid never exists.  Returns 0 for an invalid problem. */
+size_t kd_chunked_workspace_size(const kd_problem* prob);
+
+/* Static string naming a status code (never NULL). */
+const char* kd_status_string(int status);
+
+/* Forward.  Walks the n rows in chunks of prob->chunk rows; per chunk it
+ * renormalises the teacher record, runs the projection H_c W^T on matrix
+ * cores with an online per-row max / sum-of-exponentials and a gather of the
+ * student logits at the K teacher ids, then folds the chunk into the running
+ * loss.
+ *   H        [n,d]  x_dtype   hidden states
+ *   W        [v,d]  x_dtype   output projection (nn.Linear [out,in] layout)
+ *   t_ids    [n,k]  int32     cached teacher token ids
+ *   t_logits [n,k]  t_dtype   cached teacher logits (any order)
+ *   mask     [n]    uint8     0 = position ignored (its teacher record is not
+ *                             read), NULL = every position counts
+ *   loss     [1]    float     out: L (fixed-order fp64 reduction, then fp32)
+ *   lse      [n]    float     out: lse_i for every row, masked ones included
+ *   row_loss [n]    float     out (optional, NULL = skip): m_i * KL_i
+ *   zg       [n,k]  float     out (optional, NULL = skip): z_{i,t_ik}, the
+ *                             projection's own fp32 accumulator value; 0 on
+ *                             masked rows
+ * Returns KD_OK or an error status (nothing enqueued on error). */
+int kd_chunked_fwd(const kd_problem* prob, const void* H, const void* W,
+                   const int32_t* t_ids, const void* t_logits, const uint8_t* mask,
+                   float* loss, float* lse, float* row_loss, float* zg,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward.  Recomputes each chunk's logits, forms
+ *   dZ_iv = g m_i (s_i exp(z_iv - lse_i) - sum_k p_ik [t_ik = v])
+ * in fp32 and rounds it once to x_dtype (the -p terms are applied before the
+ * rounding), then dH_c = dZ_c W and dW += dZ_c^T H_c with fp32 accumulation.
+ *   H, W, t_ids, t_logits, mask   as for the forward (same values)
+ *   lse       [n]   float    the forward's lse output
+ *   grad_loss [1]   float    device scalar g (upstream gradient), NULL = 1
+ *   dH        [n,d] float    out, overwritten; masked rows are exactly zero
+ *   dW        [v,d] float    in/out, accumulated (+=); prior contents kept
+ * Returns KD_OK or an error status (nothing enqueued on error). */
+int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W,
+                   const int32_t* t_ids, const void* t_logits, const uint8_t* mask,
+                   const float* lse, const float* grad_loss, float* dH, float* dW,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KD_CHUNKED_H */

@@ -1,0 +1,62 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the HIP path
+through the C ABI binding, and compare with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+from chunked_kl_loss_row_amd import loss as L
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(arr, tag=None):
+    """Host array -> contiguous device tensor (uint16 bits -> bfloat16)."""
+    if arr is None:
+        return None
+    if tag == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def upload(inp):
+    wl = inp["wl"]
+    return {
+        "H": dev(inp["H"], wl.x_dtype),
+        "W": dev(inp["W"], wl.x_dtype),
+        "t_ids": dev(inp["t_ids"]),
+        "t_logits": dev(inp["t_logits"], wl.t_dtype),
+        "mask": dev(inp["mask"]) if inp["mask"] is not None else None,
+    }
+
+
+def run_hip(d, chunk, g=None, mask="default", dW_init=None, zg=True, row_loss=True, workspace=None):
+    """Forward + backward on the GPU; returns numpy results."""
+    m = d["mask"] if isinstance(mask, str) else mask
+    f = L.forward(d["H"], d["W"], d["t_ids"], d["t_logits"], m, chunk=chunk, row_loss=row_loss, zg=zg,
+                  workspace=workspace)
+    gl = None if g is None else torch.tensor([g], dtype=torch.float32, device="cuda")
+    dW = None if dW_init is None else dW_init.clone()
+    dH, dW = L.backward(d["H"], d["W"], d["t_ids"], d["t_logits"], m, f["lse"], gl, dW=dW, chunk=chunk,
+                        workspace=f["workspace"])
+    torch.cuda.synchronize()
+    out = {"loss": float(f["loss"].item()), "lse": f["lse"].cpu().numpy(), "dH": dH, "dW": dW}
+    if row_loss:
+        out["row_loss"] = f["row_loss"].cpu().numpy()
+    if zg:
+        out["zg"] = f["zg"].cpu().numpy()
+    return out
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def rel(a, b):
+    return abs(a - b) / max(abs(b), 1e-300)

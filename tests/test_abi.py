@@ -1,0 +1,143 @@
+"""C ABI checks that need no GPU: exports, status strings, workspace sizing,
+and argument validation (every error returns before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_kl_loss_row_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libkdchunk.so not built")
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(kd_[a-z_0-9]+)\s*\(", text, re.M))
+    return sorted(names)
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for st in range(8):
+        s = B.kd_status_string(st)
+        assert s.startswith("KD_OK" if st == 0 else "KD_ERR_")
+    assert "unknown" in B.kd_status_string(99)
+
+
+def P(n=1000, d=128, v=4096, k=16, chunk=64, x=B.KD_BF16, t=None):
+    return B.problem(n, d, v, k, chunk, x, t)
+
+
+def test_workspace_independent_of_n():
+    sizes = {B.kd_chunked_workspace_size(P(n=n)) for n in (0, 1, 64, 1000, 10 ** 9)}
+    assert len(sizes) == 1 and sizes.pop() > 0
+
+
+def test_workspace_grows_with_chunk_and_dtype():
+    a = B.kd_chunked_workspace_size(P(chunk=64))
+    b = B.kd_chunked_workspace_size(P(chunk=128))
+    c = B.kd_chunked_workspace_size(P(chunk=64, x=B.KD_F32))
+    assert a < b and a < c
+    # the chunk's dZ tile (chunk x padded V) dominates: at least chunk * V * 2 bytes
+    big = B.kd_chunked_workspace_size(P(n=32768, d=2880, v=201088, k=100, chunk=2048))
+    assert 2048 * 201088 * 2 <= big < 2 * 2048 * 201088 * 2
+
+
+@pytest.mark.parametrize("kw", [dict(n=-1), dict(d=0), dict(v=0), dict(k=0), dict(k=257, v=1000),
+                                dict(k=20, v=10), dict(chunk=0), dict(v=16777216)])
+def test_bad_shapes(kw):
+    prob = P(**kw)
+    assert B.kd_chunked_workspace_size(prob) == 0
+    st = B.kd_chunked_fwd(prob, 16, 16, 16, 16, None, 16, 16, workspace=16, workspace_bytes=1 << 40,
+                          stream=0, check=False)
+    assert st == B.KD_ERR_SHAPE
+
+
+def test_bad_dtype_and_alignment():
+    fake = 1 << 20
+    for prob, want in ((P(x=2), B.KD_ERR_DTYPE), (P(t=7), B.KD_ERR_DTYPE), (P(d=12), B.KD_ERR_ALIGN)):
+        st = B.kd_chunked_fwd(prob, fake, fake, fake, fake, None, fake, fake, workspace=fake,
+                              workspace_bytes=1 << 40, stream=0, check=False)
+        assert st == want
+    st = B.kd_chunked_fwd(P(), fake + 2, fake, fake, fake, None, fake, fake, workspace=fake,
+                          workspace_bytes=1 << 40, stream=0, check=False)
+    assert st == B.KD_ERR_ALIGN
+    st = B.kd_chunked_bwd(P(), fake, fake, fake, fake, None, fake, None, fake + 4, fake,
+                          workspace=fake, workspace_bytes=1 << 40, stream=0, check=False)
+    assert st == B.KD_ERR_ALIGN
+
+
+def test_null_pointers():
+    fake = 1 << 20
+    st = B.lib().kd_chunked_fwd(None, fake, fake, fake, fake, None, fake, fake, None, None, fake, 1 << 40, None)
+    assert st == B.KD_ERR_NULL
+    args = dict(H=fake, W=fake, t_ids=fake, t_logits=fake, lse=fake)
+    for missing in args:
+        a = dict(args)
+        a[missing] = None
+        st = B.kd_chunked_fwd(P(), a["H"], a["W"], a["t_ids"], a["t_logits"], None, fake, a["lse"],
+                              workspace=fake, workspace_bytes=1 << 40, stream=0, check=False)
+        assert st == B.KD_ERR_NULL, missing
+    st = B.kd_chunked_fwd(P(), fake, fake, fake, fake, None, None, fake, workspace=fake,
+                          workspace_bytes=1 << 40, stream=0, check=False)
+    assert st == B.KD_ERR_NULL
+    st = B.kd_chunked_bwd(P(), fake, fake, fake, fake, None, fake, None, fake, None, workspace=fake,
+                          workspace_bytes=1 << 40, stream=0, check=False)
+    assert st == B.KD_ERR_NULL
+
+
+def test_workspace_too_small():
+    fake = 1 << 20
+    need = B.kd_chunked_workspace_size(P())
+    st = B.kd_chunked_fwd(P(), fake, fake, fake, fake, None, fake, fake, workspace=fake,
+                          workspace_bytes=need - 1, stream=0, check=False)
+    assert st == B.KD_ERR_WORKSPACE
+    st = B.kd_chunked_bwd(P(), fake, fake, fake, fake, None, fake, None, fake, fake, workspace=fake,
+                          workspace_bytes=need - 1, stream=0, check=False)
+    assert st == B.KD_ERR_WORKSPACE
+
+
+@pytest.mark.skipif(_has_gpu(), reason="with a GPU present valid arguments would launch")
+def test_valid_arguments_without_gpu_report_device():
+    fake = 1 << 20
+    need = B.kd_chunked_workspace_size(P())
+    st = B.kd_chunked_fwd(P(), fake, fake, fake, fake, None, fake, fake, workspace=fake,
+                          workspace_bytes=need, stream=0, check=False)
+    assert st == B.KD_ERR_DEVICE
+    with pytest.raises(B.KDError):
+        B.kd_chunked_bwd(P(), fake, fake, fake, fake, None, fake, None, fake, fake, workspace=fake,
+                         workspace_bytes=need, stream=0)
+
+
+def test_profile_hook_without_launches():
+    assert B.kd_profile_enable(True) == 0
+    allk = B.kd_profile_all()
+    assert len(allk) == B.KD_K_COUNT and all(v == (0.0, 0) for v in allk.values())
+    assert "fwd_proj" in allk and "bwd_dw" in allk
+    with pytest.raises(B.KDError):
+        B.kd_profile_read(B.KD_K_COUNT)
+    assert B.kd_profile_enable(False) == 0
