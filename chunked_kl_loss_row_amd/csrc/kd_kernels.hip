@@ -306,8 +306,9 @@ __global__ void k_zero_loss(float* loss) { loss[0] = 0.f; }
 // backward: recompute the projection and form the closed-form dZ
 // ---------------------------------------------------------------------------
 // dZ_iv = g m_i (s_i exp(z_iv - lse_i) - sum_k p_ik [t_ik = v]), evaluated in
-// fp32 with the -p terms applied before the single rounding to the storage
-// dtype.  Columns in [v, ldz) are written as zeros (padding of the row).
+// fp32 in that order (the bracket first, then g) with the -p terms applied
+// before the single rounding to the storage dtype.  Columns in [v, ldz) are
+// written as zeros (padding of the row).
 template <typename T>
 __global__ __launch_bounds__(256, 1) void k_bwd_dz(const T* __restrict__ H, const T* __restrict__ W,
                                                    int rows, int d, int v, int nvt, int K, int ldz,
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dz(const T* __restrict__ H, cons
         lo = lb[static_cast<long>(gr) * (nvt + 1) + vt];
         hi = lb[static_cast<long>(gr) * (nvt + 1) + vt + 1];
         gm = g;
-        coef = g * ssum[gr];
+        coef = ssum[gr];
       }
     }
     s_lo[r] = lo;
@@ -374,12 +375,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dz(const T* __restrict__ H, cons
         const f32x4 x = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + c0);
         float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = live ? coef * fast_exp2(fmaf(x[e], kLog2e, -lse2)) : 0.f;
+        for (int e = 0; e < 4; ++e) o[e] = coef * fast_exp2(fmaf(x[e], kLog2e, -lse2));
         for (int q = lo; q < hi; ++q) {
           const long kq = static_cast<long>(grow) * K + q;
           const int c = static_cast<int>(keys[kq] >> 8) - vt * G::BN - c0;
           if (static_cast<unsigned>(c) < 4u) {
-            const float sub = gm * psort[kq];
+            const float sub = psort[kq];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               if (c == e) o[e] -= sub;
@@ -387,8 +388,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dz(const T* __restrict__ H, cons
         }
         const int gc = vt * G::BN + c0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (gc + e >= v) o[e] = 0.f;
+        for (int e = 0; e < 4; ++e) o[e] = (live && gc + e < v) ? gm * o[e] : 0.f;
         if constexpr (sizeof(T) == 2) {
           uint32_t lo2 = static_cast<uint32_t>(Tr::from_f32(o[0])) | (static_cast<uint32_t>(Tr::from_f32(o[1])) << 16);
           uint32_t hi2 = static_cast<uint32_t>(Tr::from_f32(o[2])) | (static_cast<uint32_t>(Tr::from_f32(o[3])) << 16);

@@ -127,6 +127,11 @@ def _distinct_rows(rng, n, k, lo, hi):
     without repeats keep their draw order, so the ids are not sorted)."""
     if hi - lo < k:
         raise ValueError("not enough ids for k distinct draws")
+    if k * k > 2 * (hi - lo):
+        # many repeats expected: take the first k entries of a random
+        # permutation of the range per row instead
+        keys = rng.random((n, hi - lo))
+        return np.argsort(keys, axis=1)[:, :k].astype(np.int64) + lo
     ids = rng.integers(lo, hi, size=(n, k), dtype=np.int64)
     todo = np.arange(n)
     while True:
