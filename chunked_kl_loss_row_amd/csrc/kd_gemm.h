@@ -1,0 +1,332 @@
+// Block-tile matrix-core GEMM engine for gfx950 (CDNA4).
+//
+// C[BM x BN] (fp32, registers) = sum over a k range of A(m, k) * B(n, k).
+// Each operand is either
+//   KC  -- k contiguous in memory: element (r, k) at ptr[r * ld + k], or
+//   KO  -- k outer:                element (r, k) at ptr[k * ld + r].
+// The four contractions of the loss use: projection (KC, KC), dH = dZ W
+// (KC, KO), dW = dZ^T H (KO, KO).
+//
+// Data movement.  Tiles go from global memory straight into LDS with
+// buffer_load ... lds (16 bytes per lane, one 1 KiB LDS block per wave
+// instruction); out-of-range lanes get an offset past the buffer's record
+// count, which the hardware turns into zeros, so bounds need no branches.
+// Each operand stage is R * 128 bytes in both layouts:
+//   KC: [R rows][128 B of k], 16-byte chunk c of row r stored at c ^ ((r>>1)&7);
+//   KO: [BK rows of k][R entries], 16-byte chunk c of row k stored at
+//       c ^ fko(k) (bf16: 4*(k&3); fp32: 8*((k>>2)&1)).
+// The swizzles make the matrix-core fragment reads bank-conflict free:
+//   KC: ds_read_b128, lane l -> row l%32, k chunk from l/32;
+//   KO bf16: ds_read_b64_tr_b16 (LDS transpose read), two per fragment;
+//   KO fp32: four ds_read_b32.
+// Two LDS stages; per k tile: wait for own loads, one barrier, issue the
+// loads of tile k+2 into the stage just consumed, compute tile k+1.
+//
+// Matrix-core atom: 32x32 output.  bf16: v_mfma_f32_32x32x16_bf16 (8 k per
+// lane); fp32: four v_mfma_f32_32x32x2_f32 (one k per lane each).  A and B
+// fragments use the same per-lane k assignment (lane group h = l/32 holds k
+// = 8h..8h+7 for bf16, 4h..4h+3 within each fp32 fragment).  Output of an
+// atom: lane l, element r -> row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kd {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+constexpr uint32_t kOOB = 0x80000000u;  // offset past every record count we set
+
+// s_waitcnt immediate that waits for at most n outstanding vector-memory
+// operations and does not wait on the other counters (gfx9 encoding).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {  // bf16 as raw bits
+  static constexpr int VEC = 8;
+  __device__ __forceinline__ static float to_f32(uint16_t v) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+  }
+  __device__ __forceinline__ static uint16_t from_f32(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // nearest even
+  }
+  __device__ __forceinline__ static void mma(f32x16& c, const u32x4& a, const u32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Elem<float> {
+  static constexpr int VEC = 4;
+  __device__ __forceinline__ static float to_f32(float v) { return v; }
+  __device__ __forceinline__ static float from_f32(float f) { return f; }
+  __device__ __forceinline__ static void mma(f32x16& c, const u32x4& a, const u32x4& b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[j]), __uint_as_float(b[j]), c, 0, 0, 0);
+  }
+};
+
+// Buffer resource (gfx9 layout): base address, stride 0, record count in
+// bytes (capped below kOOB so that offset kOOB is always out of range), and
+// the raw-buffer format word.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : static_cast<uint32_t>(bytes);
+  return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xFFFFu, n, 0x00020000u};
+}
+
+// 16 bytes per lane from the buffer into LDS at m0 + 16 * lane.  Issued as
+// inline assembly: the compiler's wait-count pass would otherwise make every
+// later LDS read wait for these loads, including those of a stage nobody is
+// reading yet.  Completion is tracked explicitly with s_waitcnt vmcnt.
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p)));
+}
+
+// One operand of a block tile.
+template <typename T>
+struct Operand {
+  const T* ptr;   // storage origin
+  long ld;        // leading dimension (elements)
+  long extent;    // elements addressable from ptr
+  int r0;         // first tile row (m or n index)
+  int r_lim;      // rows >= r_lim read as zero
+  int k_lim;      // k >= k_lim reads as zero (multiple of VEC)
+};
+
+// Loads of one operand stage, R tile rows, 4 waves.
+template <typename T, int R, bool KC>
+struct StageLoader {
+  static constexpr int VEC = Elem<T>::VEC;
+  static constexpr int SZ = static_cast<int>(sizeof(T));
+  static constexpr int BK = 128 / SZ;
+  static constexpr int NI = R / 32;           // 1 KiB wave instructions per wave per stage
+  static constexpr int CPR = R * SZ / 16;     // KO: 16-byte chunks per k row
+  static_assert(R % 32 == 0, "tile rows must be a multiple of 32");
+  static_assert(KC || (CPR % 16 == 0), "k-outer tiles need >= 256 bytes per k row");
+
+  uint32_t voff[NI];   // byte offset from the tile's base (k part excluded for KC)
+  int rk[NI];          // KC: element offset of the chunk along k; KO: k row
+  bool ok[NI];         // row (KC) / column chunk (KO) inside the operand
+
+  __device__ __forceinline__ static int fko(int k) {
+    return SZ == 2 ? 4 * (k & 3) : 8 * ((k >> 2) & 1);
+  }
+
+  __device__ __forceinline__ void init(const Operand<T>& op, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int S = (wave * NI + i) * 64 + lane;
+      if (KC) {
+        const int r = S >> 3, p = S & 7;
+        const int c = p ^ ((r >> 1) & 7);
+        voff[i] = static_cast<uint32_t>(r * op.ld * SZ + c * 16);
+        rk[i] = c * VEC;
+        ok[i] = op.r0 + r < op.r_lim;
+      } else {
+        const int k = S / CPR, p = S % CPR;
+        const int c = p ^ fko(k);
+        voff[i] = static_cast<uint32_t>(k * op.ld * SZ + c * 16);
+        rk[i] = k;
+        ok[i] = op.r0 + c * VEC < op.r_lim;
+      }
+    }
+  }
+
+  // Issue the loads of the k tile starting at k0 into LDS at `dst`.
+  __device__ __forceinline__ void issue(const Operand<T>& op, int k0, char* dst, int wave) const {
+    u32x4 rs;
+    if (KC) {
+      const long base = static_cast<long>(op.r0) * op.ld;
+      rs = make_rsrc(op.ptr + base, static_cast<uint64_t>(op.extent - base) * SZ);
+    } else {
+      const long base = static_cast<long>(k0) * op.ld + op.r0;
+      rs = make_rsrc(op.ptr + base, static_cast<uint64_t>(op.extent - base) * SZ);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      uint32_t o;
+      if (KC)
+        o = (ok[i] && k0 + rk[i] < op.k_lim) ? voff[i] + static_cast<uint32_t>(k0 * SZ) : kOOB;
+      else
+        o = (ok[i] && k0 + rk[i] < op.k_lim) ? voff[i] : kOOB;
+      lds_dma16(rs, o, lds_addr(dst + (wave * NI + i) * 1024));
+    }
+  }
+};
+
+// Fragment reads of one operand for a wave: F fragments of 32 rows at rows
+// w0 + 32 f, k step kk (16 k for bf16, 8 for fp32).
+template <typename T, int R, bool KC>
+struct FragReader {
+  static constexpr int SZ = static_cast<int>(sizeof(T));
+  __device__ __forceinline__ static u32x4 read(const char* stage, int row0, int kk, int lane) {
+    if (KC) {
+      const int r = row0 + (lane & 31);
+      const int c = 2 * kk + (lane >> 5);
+      return *(const lds_u32x4*)(stage + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+    } else if (SZ == 2) {
+      const int q = lane >> 4, s = lane & 15;
+      const int n = row0 + 16 * (q & 1) + 4 * (s & 3);
+      const int k = 16 * kk + 8 * (q >> 1) + (s >> 2);
+      const int ch = ((n >> 3) ^ (4 * (k & 3))) << 4;
+      const char* p0 = stage + k * (R * 2) + ch + ((n & 7) << 1);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * (R * 2)));
+      const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+      return u32x4{a[0], a[1], b[0], b[1]};
+    } else {
+      const int n = row0 + (lane & 31), h = lane >> 5;
+      u32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 8 * kk + 4 * h + j;
+        v[j] = *(const lds_u32*)(stage + k * (R * 4) + (((n >> 2) ^ (8 * h)) << 4) + ((n & 3) << 2));
+      }
+      return v;
+    }
+  }
+};
+
+template <typename T, int BM_, int BN_, bool A_KC, bool B_KC>
+struct Gemm {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int SZ = static_cast<int>(sizeof(T));
+  static constexpr int BK = 128 / SZ;
+  static constexpr int NT = 256;                 // 4 waves, 2 x 2
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+
+  using LA = StageLoader<T, BM, A_KC>;
+  using LB = StageLoader<T, BN, B_KC>;
+  using RA = FragReader<T, BM, A_KC>;
+  using RB = FragReader<T, BN, B_KC>;
+
+  __device__ __forceinline__ static void compute(const char* st, f32x16 (&acc)[FM][FN], int wm, int wn,
+                                                 int lane) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 af[FM], bf[FN];
+#pragma unroll
+      for (int f = 0; f < FM; ++f) af[f] = RA::read(st, wm * WM + 32 * f, kk, lane);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) bf[f] = RB::read(st + A_BYTES, wn * WN + 32 * f, kk, lane);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) Elem<T>::mma(acc[i][j], af[i], bf[j]);
+    }
+  }
+
+  // acc = sum over k in [k_begin, k_end) of A(m, k) B(n, k).  Leaves LDS free
+  // (a barrier follows the last tile).
+  __device__ __forceinline__ static void run(const Operand<T>& A, const Operand<T>& B, int k_begin, int k_end,
+                                             char* lds, f32x16 (&acc)[FM][FN]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    const int nk = (k_end - k_begin + BK - 1) / BK;
+    if (nk <= 0) {
+      __syncthreads();
+      return;
+    }
+    Operand<T> a = A, b = B;
+    a.k_lim = min(A.k_lim, k_end);
+    b.k_lim = min(B.k_lim, k_end);
+    LA la;
+    LB lb;
+    la.init(a, wave, lane);
+    lb.init(b, wave, lane);
+    la.issue(a, k_begin, lds, wave);
+    lb.issue(b, k_begin, lds + A_BYTES, wave);
+    if (nk > 1) {
+      la.issue(a, k_begin + BK, lds + STAGE, wave);
+      lb.issue(b, k_begin + BK, lds + STAGE + A_BYTES, wave);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LA::NI + LB::NI));  // the first tile has landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* cur = lds + (kt & 1) * STAGE;
+      compute(cur, acc, wm, wn, lane);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // own loads of tile kt+1 have landed
+      __syncthreads();                      // everyone: tile kt consumed, tile kt+1 visible
+      if (kt + 2 < nk) {
+        char* dst = lds + (kt & 1) * STAGE;
+        la.issue(a, k_begin + (kt + 2) * BK, dst, wave);
+        lb.issue(b, k_begin + (kt + 2) * BK, dst + A_BYTES, wave);
+      }
+    }
+  }
+};
+
+// Branch-free fp32 access to a row-major [rows][ld] region through a buffer
+// resource: offsets past the region (or kOOB) read as zero / drop the write.
+struct F32Region {
+  __amdgpu_buffer_rsrc_t rs;
+  __device__ __forceinline__ F32Region(float* base, long elems) {
+    const long bytes = elems > 0 ? elems * 4 : 0;
+    rs = __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0),
+                                           static_cast<int>(bytes > 0x7FFFFFF0L ? 0x7FFFFFF0L : bytes),
+                                           0x00020000);
+  }
+  // the b32 builtins move 32-bit integers: bit casts, not conversions
+  __device__ __forceinline__ float load(uint32_t off) const {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+  }
+  __device__ __forceinline__ void store(float x, uint32_t off) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, off, 0, 0);
+  }
+};
+
+// Workgroup -> tile mapping that keeps neighbouring tiles on one XCD.
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8); this maps
+// the ids of XCD x onto a contiguous range of the linear tile order so tiles
+// sharing operand panels share that XCD's L2.  Returns -1 for padding ids.
+__device__ __forceinline__ int xcd_tile(int bid, int total) {
+  const int per = (total + 7) / 8;
+  const int t = (bid % 8) * per + bid / 8;
+  return t < total ? t : -1;
+}
+__host__ __forceinline__ int xcd_grid(int total) { return ((total + 7) / 8) * 8; }
+
+// Output position of accumulator element e of atom (i, j) for a wave at
+// (wm, wn): row / column inside the block tile.
+template <class G>
+__device__ __forceinline__ int acc_row(int wm, int i, int e, int lane) {
+  return wm * G::WM + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+}
+template <class G>
+__device__ __forceinline__ int acc_col(int wn, int j, int lane) {
+  return wn * G::WN + 32 * j + (lane & 31);
+}
+
+}  // namespace kd

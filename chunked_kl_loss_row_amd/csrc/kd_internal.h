@@ -12,7 +12,7 @@ namespace kd {
 constexpr int kProjBM = 256;   // chunk rows per projection tile
 constexpr int kProjBN = 256;   // vocabulary entries per projection tile
 constexpr int kGradBM = 256;   // output rows per dH / dW tile
-constexpr int kGradBN = 192;   // hidden columns per dH / dW tile
+constexpr int kGradBN = 256;   // hidden columns per dH / dW tile
 constexpr int kMaxSplit = 16;  // largest split of the dH reduction over V
 
 // Everything one chunk's kernels need.  Input pointers are already offset

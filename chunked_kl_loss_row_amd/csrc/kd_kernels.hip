@@ -10,20 +10,24 @@
 // (bounded by the chunk size) and consumed by the two gradient GEMMs.
 #include <math.h>
 
-#include "kd_device.h"
+#include "kd_gemm.h"
 #include "kd_internal.h"
+#include "kd_util.h"
 
 namespace kd {
 
 template <typename T>
-using ProjGemm = Gemm<T, kProjBM, kProjBN, 2, 2, true, true>;
+using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true>;
 template <typename T>
-using DhGemm = Gemm<T, kGradBM, kGradBN, 2, 2, true, false>;
+using DhGemm = Gemm<T, kGradBM, kGradBN, true, false>;
 template <typename T>
-using DwGemm = Gemm<T, kGradBM, kGradBN, 2, 2, false, false>;
+using DwGemm = Gemm<T, kGradBM, kGradBN, false, false>;
 
-constexpr int kStageRows = 128;          // rows of the fp32 epilogue stage
-constexpr int kStagePitch = kProjBN + 4; // floats per stage row
+constexpr int kStageRows = 128;           // rows of the fp32 epilogue stage
+constexpr int kStagePitch = kProjBN + 8;  // floats per stage row (rows 4 apart hit other banks)
+constexpr int kStageBytes = kStageRows * kStagePitch * 4;
+template <class G>
+constexpr int proj_smem_bytes() { return G::LDS_BYTES > kStageBytes ? G::LDS_BYTES : kStageBytes; }
 
 // ---------------------------------------------------------------------------
 // teacher record -> renormalised distribution, id-sorted keys, tile ranges
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
       a[q] = -INFINITY;
       if (k < K) {
         key[q] = (static_cast<uint32_t>(ids[rbase + k]) << 8) | static_cast<uint32_t>(k);
-        a[q] = Traits<TT>::to_f32(logits[rbase + k]);
+        a[q] = Elem<TT>::to_f32(logits[rbase + k]);
         amax = fmaxf(amax, a[q]);
       }
     }
@@ -135,19 +139,18 @@ __global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
 // ---------------------------------------------------------------------------
 // Write the accumulators of the rows in stage half `h` to the fp32 stage.
 template <typename G>
-__device__ __forceinline__ void stage_half(float* stage, const f32x4 (&acc)[G::FM][G::FN], int h) {
+__device__ __forceinline__ void stage_half(float* stage, const f32x16 (&acc)[G::FM][G::FN], int h) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int fm = 0; fm < G::FM; ++fm) {
-    const int rb = wm * G::WM + fm * 16;
-    if (rb / kStageRows != h) continue;
+  for (int i = 0; i < G::FM; ++i) {
+    if ((wm * G::WM + 32 * i) / kStageRows != h) continue;
 #pragma unroll
-    for (int fn = 0; fn < G::FN; ++fn)
+    for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        stage[(rb - h * kStageRows + 4 * (lane >> 4) + r) * kStagePitch + wn * G::WN + fn * 16 +
-              (lane & 15)] = acc[fm][fn][r];
+      for (int e = 0; e < 16; ++e)
+        stage[(acc_row<G>(wm, i, e, lane) - h * kStageRows) * kStagePitch + acc_col<G>(wn, j, lane)] =
+            acc[i][j][e];
   }
 }
 
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_proj(const T* __restrict__ H, co
                                                      float* __restrict__ zgs, float* __restrict__ pm,
                                                      float* __restrict__ ps) {
   using G = ProjGemm<T>;
-  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
   const int rtn = (rows + G::BM - 1) / G::BM;
   const int t = xcd_tile(blockIdx.x, rtn * nvt);
@@ -184,8 +187,10 @@ __global__ __launch_bounds__(256, 1) void k_fwd_proj(const T* __restrict__ H, co
     s_lo[r] = lo;
     s_hi[r] = hi;
   }
-  f32x4 acc[G::FM][G::FN];
-  G::run(H, d, rt * G::BM, rows, d, W, d, vt * G::BN, v, d, 0, d, reinterpret_cast<T*>(smem), acc);
+  f32x16 acc[G::FM][G::FN];
+  const Operand<T> A{H, d, static_cast<long>(rows) * d, rt * G::BM, rows, d};
+  const Operand<T> B{W, d, static_cast<long>(v) * d, vt * G::BN, v, d};
+  G::run(A, B, 0, d, smem, acc);
 
   float* stage = reinterpret_cast<float*>(smem);
   const int ncols = min(G::BN, v - vt * G::BN);
@@ -320,8 +325,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dz(const T* __restrict__ H, cons
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ gptr, T* __restrict__ dz) {
   using G = ProjGemm<T>;
-  using Tr = Traits<T>;
-  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  using Tr = Elem<T>;
+  __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
   __shared__ float s_lse2[G::BM], s_coef[G::BM], s_gm[G::BM];
   __shared__ int s_live[G::BM];
@@ -353,8 +358,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dz(const T* __restrict__ H, cons
     s_gm[r] = gm;
     s_live[r] = live;
   }
-  f32x4 acc[G::FM][G::FN];
-  G::run(H, d, rt * G::BM, rows, d, W, d, vt * G::BN, v, d, 0, d, reinterpret_cast<T*>(smem), acc);
+  f32x16 acc[G::FM][G::FN];
+  const Operand<T> A{H, d, static_cast<long>(rows) * d, rt * G::BM, rows, d};
+  const Operand<T> B{W, d, static_cast<long>(v) * d, vt * G::BN, v, d};
+  G::run(A, B, 0, d, smem, acc);
 
   float* stage = reinterpret_cast<float*>(smem);
   const int g16 = tid >> 4, l16 = tid & 15;
@@ -418,20 +425,26 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dh(const T* __restrict__ dz, int
   const int ks = t / (mtn * ntn), rem = t % (mtn * ntn);
   const int mt = rem / ntn, nt = rem % ntn;
   const int k0 = ks * kslice, k1 = min(ldz, k0 + kslice);
-  f32x4 acc[G::FM][G::FN];
-  G::run(dz, ldz, mt * G::BM, rows, ldz, W, d, nt * G::BN, d, v, k0, k1, reinterpret_cast<T*>(smem), acc);
-  float* o = out + ks * split_stride;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / 2, wn = wave % 2;
+  f32x16 acc[G::FM][G::FN];
+  // A(m = chunk row, k = vocab) = dZ[m][k];  B(n = hidden, k = vocab) = W[k][n]
+  const Operand<T> A{dz, ldz, static_cast<long>(rows) * ldz, mt * G::BM, rows, ldz};
+  const Operand<T> B{W, d, static_cast<long>(v) * d, nt * G::BN, d, v};
+  G::run(A, B, k0, k1, smem, acc);
+  // rows past the chunk fall outside the region; columns past d get kOOB
+  const int row0 = mt * G::BM, col0 = nt * G::BN;
+  const F32Region o(out + ks * split_stride + static_cast<long>(row0) * d, static_cast<long>(rows - row0) * d);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int fm = 0; fm < G::FM; ++fm)
+  for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-    for (int fn = 0; fn < G::FN; ++fn)
+    for (int j = 0; j < G::FN; ++j) {
+      const int col = col0 + acc_col<G>(wn, j, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = mt * G::BM + wm * G::WM + fm * 16 + 4 * (lane >> 4) + r;
-        const int col = nt * G::BN + wn * G::WN + fn * 16 + (lane & 15);
-        if (row < rows && col < d) o[static_cast<long>(row) * d + col] = acc[fm][fn][r];
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t off = col < d ? static_cast<uint32_t>((acc_row<G>(wm, i, e, lane) * d + col) * 4) : kOOB;
+        o.store(acc[i][j][e], off);
       }
+    }
 }
 
 __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ part, int split,
@@ -454,24 +467,34 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dw(const T* __restrict__ dz, int
   const int t = xcd_tile(blockIdx.x, mtn * ntn);
   if (t < 0) return;
   const int mt = t / ntn, nt = t % ntn;
-  f32x4 acc[G::FM][G::FN];
+  f32x16 acc[G::FM][G::FN];
   // A(m = vocab, k = chunk row) = dZ[k][m];  B(n = hidden, k = chunk row) = H[k][n]
-  G::run(dz, ldz, mt * G::BM, ldz, rows, Hc, d, nt * G::BN, d, rows, 0, rows,
-         reinterpret_cast<T*>(smem), acc);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / 2, wn = wave % 2;
+  const Operand<T> A{dz, ldz, static_cast<long>(rows) * ldz, mt * G::BM, ldz, rows};
+  const Operand<T> B{Hc, d, static_cast<long>(rows) * d, nt * G::BN, d, rows};
+  G::run(A, B, 0, rows, smem, acc);
+  // dW += acc: all reads of a 32-row block are issued before its adds and
+  // writes; rows past v fall outside the region, columns past d get kOOB.
+  const int row0 = mt * G::BM, col0 = nt * G::BN;
+  const F32Region o(dW + static_cast<long>(row0) * d, static_cast<long>(v - row0) * d);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int fm = 0; fm < G::FM; ++fm)
+  for (int i = 0; i < G::FM; ++i) {
+    uint32_t off[G::FN][16];
+    float old[G::FN][16];
 #pragma unroll
-    for (int fn = 0; fn < G::FN; ++fn)
+    for (int j = 0; j < G::FN; ++j) {
+      const int col = col0 + acc_col<G>(wn, j, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = mt * G::BM + wm * G::WM + fm * 16 + 4 * (lane >> 4) + r;
-        const int col = nt * G::BN + wn * G::WN + fn * 16 + (lane & 15);
-        if (row < v && col < d) {
-          float* p = dW + static_cast<long>(row) * d + col;
-          *p = *p + acc[fm][fn][r];
-        }
+      for (int e = 0; e < 16; ++e) {
+        off[j][e] = col < d ? static_cast<uint32_t>((acc_row<G>(wm, i, e, lane) * d + col) * 4) : kOOB;
+        old[j][e] = o.load(off[j][e]);
       }
+    }
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o.store(old[j][e] + acc[i][j][e], off[j][e]);
+  }
 }
 
 // ---------------------------------------------------------------------------
