@@ -11,16 +11,21 @@
 // buffer_load ... lds (16 bytes per lane, one 1 KiB LDS block per wave
 // instruction); out-of-range lanes get an offset past the buffer's record
 // count, which the hardware turns into zeros, so bounds need no branches.
-// Each operand stage is R * 128 bytes in both layouts:
-//   KC: [R rows][128 B of k], 16-byte chunk c of row r stored at c ^ ((r>>1)&7);
+// A k tile holds 64 bytes of k per tile row (32 bf16 / 16 fp32), so each
+// operand stage is R * 64 bytes in both layouts:
+//   KC: [R rows][64 B of k], 16-byte chunk c of row r stored at c ^ ((r>>2)&3);
 //   KO: [BK rows of k][R entries], 16-byte chunk c of row k stored at
 //       c ^ fko(k) (bf16: 4*(k&3); fp32: 8*((k>>2)&1)).
 // The swizzles make the matrix-core fragment reads bank-conflict free:
 //   KC: ds_read_b128, lane l -> row l%32, k chunk from l/32;
 //   KO bf16: ds_read_b64_tr_b16 (LDS transpose read), two per fragment;
 //   KO fp32: four ds_read_b32.
-// Two LDS stages; per k tile: wait for own loads, one barrier, issue the
-// loads of tile k+2 into the stage just consumed, compute tile k+1.
+// Eight waves (two per SIMD, 2 x 4 grid of 128 x 64 wave tiles by default),
+// so one wave's LDS or barrier wait is covered by the other's MFMAs.
+// NS = 4 LDS stages: the loads of tile k+3 are issued while tile k is
+// computed, so each load has three compute phases to land.  One barrier per
+// tile; the first fragments of the next tile are read right after it while
+// the last MFMAs of the current tile (operands already in registers) run.
 //
 // Matrix-core atom: 32x32 output.  bf16: v_mfma_f32_32x32x16_bf16 (8 k per
 // lane); fp32: four v_mfma_f32_32x32x2_f32 (one k per lane each).  A and B
@@ -90,11 +95,19 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint64_t bytes) {
 // inline assembly: the compiler's wait-count pass would otherwise make every
 // later LDS read wait for these loads, including those of a stage nobody is
 // reading yet.  Completion is tracked explicitly with s_waitcnt vmcnt.
+// The LDS address is bound to m0 through a register constraint, so the
+// compiler materialises m0 itself.
 __device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+
+// Workgroup barrier that orders LDS only: the fences lower to
+// s_waitcnt lgkmcnt(0), so global->LDS loads of later tiles stay in flight
+// (a full __syncthreads() would wait for every outstanding vector-memory op).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -112,15 +125,15 @@ struct Operand {
   int k_lim;      // k >= k_lim reads as zero (multiple of VEC)
 };
 
-// Loads of one operand stage, R tile rows, 4 waves.
-template <typename T, int R, bool KC>
+// Loads of one operand stage, R tile rows, NWAVES waves.
+template <typename T, int R, bool KC, int NWAVES>
 struct StageLoader {
   static constexpr int VEC = Elem<T>::VEC;
   static constexpr int SZ = static_cast<int>(sizeof(T));
-  static constexpr int BK = 128 / SZ;
-  static constexpr int NI = R / 32;           // 1 KiB wave instructions per wave per stage
+  static constexpr int BK = 64 / SZ;
+  static constexpr int NI = R * 64 / 1024 / NWAVES;  // 1 KiB wave instructions per wave per stage
   static constexpr int CPR = R * SZ / 16;     // KO: 16-byte chunks per k row
-  static_assert(R % 32 == 0, "tile rows must be a multiple of 32");
+  static_assert(R * 64 % (1024 * NWAVES) == 0, "stage must split evenly over the waves");
   static_assert(KC || (CPR % 16 == 0), "k-outer tiles need >= 256 bytes per k row");
 
   uint32_t voff[NI];   // byte offset from the tile's base (k part excluded for KC)
@@ -136,8 +149,8 @@ struct StageLoader {
     for (int i = 0; i < NI; ++i) {
       const int S = (wave * NI + i) * 64 + lane;
       if (KC) {
-        const int r = S >> 3, p = S & 7;
-        const int c = p ^ ((r >> 1) & 7);
+        const int r = S >> 2, p = S & 3;
+        const int c = p ^ ((r >> 2) & 3);
         voff[i] = static_cast<uint32_t>(r * op.ld * SZ + c * 16);
         rk[i] = c * VEC;
         ok[i] = op.r0 + r < op.r_lim;
@@ -151,18 +164,22 @@ struct StageLoader {
     }
   }
 
-  // Issue the loads of the k tile starting at k0 into LDS at `dst`.
-  __device__ __forceinline__ void issue(const Operand<T>& op, int k0, char* dst, int wave) const {
-    u32x4 rs;
+  // Buffer resource of the k tile starting at k0 (wave-uniform).
+  __device__ __forceinline__ u32x4 rsrc(const Operand<T>& op, int k0) const {
     if (KC) {
       const long base = static_cast<long>(op.r0) * op.ld;
-      rs = make_rsrc(op.ptr + base, static_cast<uint64_t>(op.extent - base) * SZ);
-    } else {
-      const long base = static_cast<long>(k0) * op.ld + op.r0;
-      rs = make_rsrc(op.ptr + base, static_cast<uint64_t>(op.extent - base) * SZ);
+      return make_rsrc(op.ptr + base, static_cast<uint64_t>(op.extent - base) * SZ);
     }
+    const long base = static_cast<long>(k0) * op.ld + op.r0;
+    return make_rsrc(op.ptr + base, static_cast<uint64_t>(op.extent - base) * SZ);
+  }
+
+  // Issue instructions [I0, I1) of the k tile starting at k0 into LDS `dst`.
+  template <int I0, int I1>
+  __device__ __forceinline__ void issue(const Operand<T>& op, const u32x4& rs, int k0, char* dst,
+                                        int wave) const {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int i = I0; i < I1; ++i) {
       uint32_t o;
       if (KC)
         o = (ok[i] && k0 + rk[i] < op.k_lim) ? voff[i] + static_cast<uint32_t>(k0 * SZ) : kOOB;
@@ -171,10 +188,13 @@ struct StageLoader {
       lds_dma16(rs, o, lds_addr(dst + (wave * NI + i) * 1024));
     }
   }
+  __device__ __forceinline__ void issue_all(const Operand<T>& op, int k0, char* dst, int wave) const {
+    issue<0, NI>(op, rsrc(op, k0), k0, dst, wave);
+  }
 };
 
-// Fragment reads of one operand for a wave: F fragments of 32 rows at rows
-// w0 + 32 f, k step kk (16 k for bf16, 8 for fp32).
+// Fragment read of one operand for a wave: 32 tile rows from row0, k step
+// kk (16 k for bf16, 8 for fp32; two steps per k tile).
 template <typename T, int R, bool KC>
 struct FragReader {
   static constexpr int SZ = static_cast<int>(sizeof(T));
@@ -182,7 +202,7 @@ struct FragReader {
     if (KC) {
       const int r = row0 + (lane & 31);
       const int c = 2 * kk + (lane >> 5);
-      return *(const lds_u32x4*)(stage + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+      return *(const lds_u32x4*)(stage + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
     } else if (SZ == 2) {
       const int q = lane >> 4, s = lane & 15;
       const int n = row0 + 16 * (q & 1) + 4 * (s & 3);
@@ -206,46 +226,64 @@ struct FragReader {
   }
 };
 
-template <typename T, int BM_, int BN_, bool A_KC, bool B_KC>
+template <typename T, int BM_, int BN_, bool A_KC, bool B_KC, int WAVES_M = 2, int WAVES_N = 4>
 struct Gemm {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int SZ = static_cast<int>(sizeof(T));
-  static constexpr int BK = 128 / SZ;
-  static constexpr int NT = 256;                 // 4 waves, 2 x 2
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int BK = 64 / SZ;             // k per tile
+  static constexpr int NS = 4;                   // LDS stages
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = 64 * NWAVES;         // two waves per SIMD by default
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int LDS_BYTES = NS * STAGE;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 
-  using LA = StageLoader<T, BM, A_KC>;
-  using LB = StageLoader<T, BN, B_KC>;
+  using LA = StageLoader<T, BM, A_KC, NWAVES>;
+  using LB = StageLoader<T, BN, B_KC, NWAVES>;
   using RA = FragReader<T, BM, A_KC>;
   using RB = FragReader<T, BN, B_KC>;
+  static constexpr int NI = LA::NI + LB::NI;     // load instructions per wave per tile
 
-  __device__ __forceinline__ static void compute(const char* st, f32x16 (&acc)[FM][FN], int wm, int wn,
-                                                 int lane) {
+  struct Frags {
+    u32x4 a[FM], b[FN];
+  };
+  __device__ __forceinline__ static void read(Frags& f, const char* st, int kk, int wm, int wn, int lane) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4 af[FM], bf[FN];
+    for (int i = 0; i < FM; ++i) f.a[i] = RA::read(st, wm * WM + 32 * i, kk, lane);
 #pragma unroll
-      for (int f = 0; f < FM; ++f) af[f] = RA::read(st, wm * WM + 32 * f, kk, lane);
+    for (int j = 0; j < FN; ++j) f.b[j] = RB::read(st + A_BYTES, wn * WN + 32 * j, kk, lane);
+  }
+  __device__ __forceinline__ static void mma(f32x16 (&acc)[FM][FN], const Frags& f) {
 #pragma unroll
-      for (int f = 0; f < FN; ++f) bf[f] = RB::read(st + A_BYTES, wn * WN + 32 * f, kk, lane);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Elem<T>::mma(acc[i][j], af[i], bf[j]);
-    }
+      for (int j = 0; j < FN; ++j) Elem<T>::mma(acc[i][j], f.a[i], f.b[j]);
+  }
+  // wait until at most `tiles` tiles of this wave's loads are in flight
+  __device__ __forceinline__ static void wait_tiles(int tiles) {
+    if (tiles >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
+    else if (tiles == 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
   // acc = sum over k in [k_begin, k_end) of A(m, k) B(n, k).  Leaves LDS free
   // (a barrier follows the last tile).
+  //   prologue: tiles 0..NS-2 in flight, wait for tile 0, barrier, read the
+  //             fragments of tile 0 step 0;
+  //   tile kt:  issue tile kt+NS-1 into the stage tile kt-1 used; read step
+  //             1 fragments; MFMAs of step 0; wait for own loads of tile
+  //             kt+1; barrier; read step 0 fragments of tile kt+1; MFMAs of
+  //             step 1 of tile kt.
   __device__ __forceinline__ static void run(const Operand<T>& A, const Operand<T>& B, int k_begin, int k_end,
                                              char* lds, f32x16 (&acc)[FM][FN]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -264,27 +302,39 @@ struct Gemm {
     LB lb;
     la.init(a, wave, lane);
     lb.init(b, wave, lane);
-    la.issue(a, k_begin, lds, wave);
-    lb.issue(b, k_begin, lds + A_BYTES, wave);
-    if (nk > 1) {
-      la.issue(a, k_begin + BK, lds + STAGE, wave);
-      lb.issue(b, k_begin + BK, lds + STAGE + A_BYTES, wave);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LA::NI + LB::NI));  // the first tile has landed
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const char* cur = lds + (kt & 1) * STAGE;
-      compute(cur, acc, wm, wn, lane);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // own loads of tile kt+1 have landed
-      __syncthreads();                      // everyone: tile kt consumed, tile kt+1 visible
-      if (kt + 2 < nk) {
-        char* dst = lds + (kt & 1) * STAGE;
-        la.issue(a, k_begin + (kt + 2) * BK, dst, wave);
-        lb.issue(b, k_begin + (kt + 2) * BK, dst + A_BYTES, wave);
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t) {
+      if (t < nk) {
+        la.issue_all(a, k_begin + t * BK, lds + t * STAGE, wave);
+        lb.issue_all(b, k_begin + t * BK, lds + t * STAGE + A_BYTES, wave);
       }
     }
+    wait_tiles(min(NS - 2, nk - 1));
+    lds_barrier();
+    Frags f0, f1;
+    read(f0, lds, 0, wm, wn, lane);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* cur = lds + (kt % NS) * STAGE;
+      if (kt + NS - 1 < nk) {
+        char* dst = lds + ((kt + NS - 1) % NS) * STAGE;
+        la.issue_all(a, k_begin + (kt + NS - 1) * BK, dst, wave);
+        lb.issue_all(b, k_begin + (kt + NS - 1) * BK, dst + A_BYTES, wave);
+      }
+      // The scheduling fences keep each step's fragment reads ahead of the
+      // MFMAs of the previous step (left alone, the scheduler sinks them
+      // next to their consumers and exposes the LDS latency every step).
+      read(f1, cur, 1, wm, wn, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(acc, f0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_tiles(min(NS - 2, nk - kt - 2));  // tile kt+1 has landed (own loads)
+      lds_barrier();                          // tile kt+1 visible; stage of kt free
+      if (kt + 1 < nk) read(f0, lds + ((kt + 1) % NS) * STAGE, 0, wm, wn, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(acc, f1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
   }
 };
 

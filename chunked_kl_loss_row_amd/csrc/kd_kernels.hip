@@ -18,6 +18,8 @@ namespace kd {
 
 template <typename T>
 using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true>;
+static_assert(Gemm<uint16_t, kProjBM, kProjBN, true, true>::NT == Gemm<float, kProjBM, kProjBN, true, true>::NT,
+              "one block size per kernel for both dtypes");
 template <typename T>
 using DhGemm = Gemm<T, kGradBM, kGradBN, true, false>;
 template <typename T>
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
 template <typename G>
 __device__ __forceinline__ void stage_half(float* stage, const f32x16 (&acc)[G::FM][G::FN], int h) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (G::BN / G::WN), wn = wave % (G::BN / G::WN);
 #pragma unroll
   for (int i = 0; i < G::FM; ++i) {
     if ((wm * G::WM + 32 * i) / kStageRows != h) continue;
@@ -163,7 +165,7 @@ __device__ __forceinline__ void stage_half(float* stage, const f32x16 (&acc)[G::
 // (the gather is a copy of the accumulator, bit for bit).  Logits never reach
 // HBM.
 template <typename T>
-__global__ __launch_bounds__(256, 1) void k_fwd_proj(const T* __restrict__ H, const T* __restrict__ W,
+__global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, const T* __restrict__ W,
                                                      int rows, int d, int v, int nvt, int K,
                                                      const uint16_t* __restrict__ lb,
                                                      const uint32_t* __restrict__ keys,
@@ -315,7 +317,7 @@ __global__ void k_zero_loss(float* loss) { loss[0] = 0.f; }
 // before the single rounding to the storage dtype.  Columns in [v, ldz) are
 // written as zeros (padding of the row).
 template <typename T>
-__global__ __launch_bounds__(256, 1) void k_bwd_dz(const T* __restrict__ H, const T* __restrict__ W,
+__global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, const T* __restrict__ W,
                                                    int rows, int d, int v, int nvt, int K, int ldz,
                                                    const uint16_t* __restrict__ lb,
                                                    const uint32_t* __restrict__ keys,
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dz(const T* __restrict__ H, cons
 // backward: dH = dZ W (split over V, fixed-order reduce) and dW += dZ^T H
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256, 1) void k_bwd_dh(const T* __restrict__ dz, int ldz,
+__global__ __launch_bounds__(512, 1) void k_bwd_dh(const T* __restrict__ dz, int ldz,
                                                    const T* __restrict__ W, int rows, int d, int v,
                                                    int split, int kslice, float* __restrict__ out,
                                                    long split_stride) {
@@ -433,7 +435,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dh(const T* __restrict__ dz, int
   // rows past the chunk fall outside the region; columns past d get kOOB
   const int row0 = mt * G::BM, col0 = nt * G::BN;
   const F32Region o(out + ks * split_stride + static_cast<long>(row0) * d, static_cast<long>(rows - row0) * d);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / (G::BN / G::WN), wn = wave % (G::BN / G::WN);
 #pragma unroll
   for (int i = 0; i < G::FM; ++i)
 #pragma unroll
@@ -458,7 +461,7 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
 }
 
 template <typename T>
-__global__ __launch_bounds__(256, 1) void k_bwd_dw(const T* __restrict__ dz, int ldz,
+__global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int ldz,
                                                    const T* __restrict__ Hc, int rows, int d, int v,
                                                    float* __restrict__ dW) {
   using G = DwGemm<T>;
@@ -476,7 +479,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dw(const T* __restrict__ dz, int
   // writes; rows past v fall outside the region, columns past d get kOOB.
   const int row0 = mt * G::BM, col0 = nt * G::BN;
   const F32Region o(dW + static_cast<long>(row0) * d, static_cast<long>(v - row0) * d);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / (G::BN / G::WN), wn = wave % (G::BN / G::WN);
 #pragma unroll
   for (int i = 0; i < G::FM; ++i) {
     uint32_t off[G::FN][16];
@@ -533,7 +537,7 @@ void launch_prep(const ChunkArgs& a, hipStream_t s) {
 
 void launch_fwd_proj(const ChunkArgs& a, hipStream_t s) {
   const int rtn = (a.rows + kProjBM - 1) / kProjBM;
-  const dim3 grid(xcd_grid(rtn * a.nvt)), block(256);
+  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
   if (a.x_bf16)
     k_fwd_proj<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
                                                 static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v,
@@ -558,7 +562,7 @@ void launch_zero_loss(float* loss, hipStream_t s) { k_zero_loss<<<dim3(1), dim3(
 
 void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s) {
   const int rtn = (a.rows + kProjBM - 1) / kProjBM;
-  const dim3 grid(xcd_grid(rtn * a.nvt)), block(256);
+  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
   if (a.x_bf16)
     k_bwd_dz<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
                                               static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
@@ -573,7 +577,7 @@ void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStre
 void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s) {
   const int mtn = (a.rows + kGradBM - 1) / kGradBM, ntn = (a.d + kGradBN - 1) / kGradBN;
   const int split = a.dh_split;
-  const dim3 grid(xcd_grid(mtn * ntn * split)), block(256);
+  const dim3 grid(xcd_grid(mtn * ntn * split)), block(DhGemm<uint16_t>::NT);
   float* out = split == 1 ? dH : a.dhp;
   const long stride = static_cast<long>(a.rows) * a.d;
   if (a.x_bf16)
@@ -596,7 +600,7 @@ void launch_dh_reduce(const ChunkArgs& a, float* dH, hipStream_t s) {
 
 void launch_bwd_dw(const ChunkArgs& a, float* dW, hipStream_t s) {
   const int mtn = (a.v + kGradBM - 1) / kGradBM, ntn = (a.d + kGradBN - 1) / kGradBN;
-  const dim3 grid(xcd_grid(mtn * ntn)), block(256);
+  const dim3 grid(xcd_grid(mtn * ntn)), block(DwGemm<uint16_t>::NT);
   if (a.x_bf16)
     k_bwd_dw<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.dz), a.ldz,
                                               static_cast<const uint16_t*>(a.H), a.rows, a.d, a.v, dW);
