@@ -475,29 +475,34 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
   const Operand<T> A{dz, ldz, static_cast<long>(rows) * ldz, mt * G::BM, ldz, rows};
   const Operand<T> B{Hc, d, static_cast<long>(rows) * d, nt * G::BN, d, rows};
   G::run(A, B, 0, rows, smem, acc);
-  // dW += acc: all reads of a 32-row block are issued before its adds and
-  // writes; rows past v fall outside the region, columns past d get kOOB.
+  // dW += acc, software pipelined over 32-row blocks: the reads of block
+  // i+1 are in flight while block i is added and written.  Rows past v fall
+  // outside the region; columns past d get kOOB.
   const int row0 = mt * G::BM, col0 = nt * G::BN;
   const F32Region o(dW + static_cast<long>(row0) * d, static_cast<long>(v - row0) * d);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / (G::BN / G::WN), wn = wave % (G::BN / G::WN);
+  auto offset = [&](int i, int j, int e) -> uint32_t {
+    const int col = col0 + acc_col<G>(wn, j, lane);
+    return col < d ? static_cast<uint32_t>((acc_row<G>(wm, i, e, lane) * d + col) * 4) : kOOB;
+  };
+  float old[2][G::FN][16];
+#pragma unroll
+  for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) old[0][j][e] = o.load(offset(0, j, e));
 #pragma unroll
   for (int i = 0; i < G::FM; ++i) {
-    uint32_t off[G::FN][16];
-    float old[G::FN][16];
+    if (i + 1 < G::FM) {
 #pragma unroll
-    for (int j = 0; j < G::FN; ++j) {
-      const int col = col0 + acc_col<G>(wn, j, lane);
+      for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        off[j][e] = col < d ? static_cast<uint32_t>((acc_row<G>(wm, i, e, lane) * d + col) * 4) : kOOB;
-        old[j][e] = o.load(off[j][e]);
-      }
+        for (int e = 0; e < 16; ++e) old[(i + 1) & 1][j][e] = o.load(offset(i + 1, j, e));
     }
 #pragma unroll
     for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o.store(old[j][e] + acc[i][j][e], off[j][e]);
+      for (int e = 0; e < 16; ++e) o.store(old[i & 1][j][e] + acc[i][j][e], offset(i, j, e));
   }
 }
 
