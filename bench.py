@@ -46,8 +46,45 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
-                    help="JSON file with rocprofv3 FETCH/WRITE traffic of the dominant kernel")
+                    help="rocprofv3 FETCH_SIZE/WRITE_SIZE summary of the dominant kernel "
+                         "(default: profiles/kd_<kernel>_<workload>_traffic.txt)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy (y = -x, fp32) of this many MiB before warm-up: "
+                         "the known-size dispatch that scales the memory counters of a --pmc run")
     return ap.parse_args()
+
+
+def source_digest():
+    """sha256 over the kernel sources: a traffic summary is valid only for the code it was taken on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "chunked_kl_loss_row_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(path, kernel):
+    """HBM bytes per launch from a committed counter summary, or None when it is missing,
+    names another kernel or was taken on other kernel sources."""
+    if not path or not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel") != kernel or fields.get("source_digest") != source_digest():
+        return None
+    try:
+        return int(float(fields["scaled_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(inp, rows_n):
@@ -108,6 +145,17 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
+    if args.copy_mib > 0:
+        # plain copy of known size: FETCH_SIZE / WRITE_SIZE of this dispatch over
+        # 2^20 * copy_mib bytes is the scale factor of the counters
+        x = torch.ones(args.copy_mib * 2 ** 18, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        del x, y
+        torch.cuda.empty_cache()
+
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     H, W = dev(inp["H"], wl.x_dtype), dev(inp["W"], wl.x_dtype)
@@ -151,18 +199,27 @@ def main():
     peak = PEAK_BF16_TFLOPS if wl.x_dtype == "bf16" else PEAK_F32_TFLOPS
     kernels = {k: {"avg_ms": (t / n if n else None), "launches_per_step": n / args.steps,
                    "ms_per_step": t / args.steps} for k, (t, n) in kern.items()}
+    # the two stand-alone (memory-bound) passes: algorithmic bytes per step and GB/s
+    ts = 2 if wl.t_dtype == "bf16" else 4
+    nvt = -(-V // 256)
+    alg_bytes = {
+        # ids + logits + mask read; sorted (key, p), zeroed gather slots, negent, s, tile bounds written
+        "prep": 2 * (N * wl.k * (4 + ts) + N + N * wl.k * 12 + N * 8 + N * (nvt + 1) * 2),
+        # tile partials (max, sum) + sorted p + gathered z + negent, s, mask read; lse, row loss written
+        "merge": N * nvt * 8 + N * wl.k * 8 + N * 9 + N * 12,
+    }
+    for k, b in alg_bytes.items():
+        if k in kernels and kernels[k]["ms_per_step"] > 0:
+            kernels[k]["alg_bytes_per_step"] = b
+            kernels[k]["GB_s"] = round(b / (kernels[k]["ms_per_step"] * 1e-3) / 1e9, 1)
     dom = max(kern, key=lambda k: kern[k][0])
     roofline = None
     if dom in GEMM_KINDS and kern[dom][1] > 0:
         per_launch_flop = 2.0 * N * D * V / (kern[dom][1] / args.steps)
         avg_s = kern[dom][0] / kern[dom][1] * 1e-3
         ach = per_launch_flop / avg_s / 1e12
-        traffic = None
-        if args.traffic and os.path.exists(args.traffic):
-            with open(args.traffic) as f:
-                tr = json.load(f)
-            if tr.get("kernel") == dom:
-                traffic = tr.get("bytes_per_launch")
+        tpath = args.traffic or os.path.join(ROOT, "profiles", f"kd_{dom}_{wl.name}_traffic.txt")
+        traffic = read_traffic(tpath, dom)
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
                     "algorithmic_flop_per_launch": per_launch_flop, "avg_launch_ms": round(avg_s * 1e3, 4)}

@@ -226,12 +226,12 @@ struct FragReader {
   }
 };
 
-template <typename T, int BM_, int BN_, bool A_KC, bool B_KC, int WAVES_M = 2, int WAVES_N = 4>
+template <typename T, int BM_, int BN_, bool A_KC, bool B_KC, int WAVES_M = 2, int WAVES_N = 4, int NS_ = 4>
 struct Gemm {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int SZ = static_cast<int>(sizeof(T));
   static constexpr int BK = 64 / SZ;             // k per tile
-  static constexpr int NS = 4;                   // LDS stages
+  static constexpr int NS = NS_;                 // LDS stages
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NWAVES;         // two waves per SIMD by default
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -264,7 +264,10 @@ struct Gemm {
   }
   // wait until at most `tiles` tiles of this wave's loads are in flight
   __device__ __forceinline__ static void wait_tiles(int tiles) {
-    if (tiles >= 2)
+    static_assert(NS <= 5 && 3 * NI < 64, "vmcnt holds at most 63");
+    if (NS >= 5 && tiles >= 3)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
+    else if (tiles >= 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
     else if (tiles == 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
