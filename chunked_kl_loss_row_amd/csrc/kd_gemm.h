@@ -232,6 +232,7 @@ struct Gemm {
   static constexpr int SZ = static_cast<int>(sizeof(T));
   static constexpr int BK = 64 / SZ;             // k per tile
   static constexpr int NS = NS_;                 // LDS stages
+  static constexpr bool EARLY = false;           // refill a stage right after the barrier that frees it
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NWAVES;         // two waves per SIMD by default
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -264,10 +265,12 @@ struct Gemm {
   }
   // wait until at most `tiles` tiles of this wave's loads are in flight
   __device__ __forceinline__ static void wait_tiles(int tiles) {
-    static_assert(NS <= 5 && 3 * NI < 64, "vmcnt holds at most 63");
-    if (NS >= 5 && tiles >= 3)
+    static_assert(NS <= 5 && 4 * NI < 64, "vmcnt holds at most 63");
+    if (tiles >= 4)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * NI));
+    else if (tiles == 3)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
-    else if (tiles >= 2)
+    else if (tiles == 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
     else if (tiles == 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
@@ -305,20 +308,21 @@ struct Gemm {
     LB lb;
     la.init(a, wave, lane);
     lb.init(b, wave, lane);
+    constexpr int PRO = EARLY ? NS : NS - 1;  // tiles in flight before the first MFMA
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t) {
+    for (int t = 0; t < PRO; ++t) {
       if (t < nk) {
         la.issue_all(a, k_begin + t * BK, lds + t * STAGE, wave);
         lb.issue_all(b, k_begin + t * BK, lds + t * STAGE + A_BYTES, wave);
       }
     }
-    wait_tiles(min(NS - 2, nk - 1));
+    wait_tiles(min(PRO - 1, nk - 1));
     lds_barrier();
     Frags f0, f1;
     read(f0, lds, 0, wm, wn, lane);
     for (int kt = 0; kt < nk; ++kt) {
       const char* cur = lds + (kt % NS) * STAGE;
-      if (kt + NS - 1 < nk) {
+      if (!EARLY && kt + NS - 1 < nk) {
         char* dst = lds + ((kt + NS - 1) % NS) * STAGE;
         la.issue_all(a, k_begin + (kt + NS - 1) * BK, dst, wave);
         lb.issue_all(b, k_begin + (kt + NS - 1) * BK, dst + A_BYTES, wave);
@@ -332,6 +336,11 @@ struct Gemm {
       __builtin_amdgcn_sched_barrier(0);
       wait_tiles(min(NS - 2, nk - kt - 2));  // tile kt+1 has landed (own loads)
       lds_barrier();                          // tile kt+1 visible; stage of kt free
+      if (EARLY && kt + NS < nk) {
+        char* dst = lds + (kt % NS) * STAGE;
+        la.issue_all(a, k_begin + (kt + NS) * BK, dst, wave);
+        lb.issue_all(b, k_begin + (kt + NS) * BK, dst + A_BYTES, wave);
+      }
       if (kt + 1 < nk) read(f0, lds + ((kt + 1) % NS) * STAGE, 0, wm, wn, lane);
       __builtin_amdgcn_sched_barrier(0);
       mma(acc, f1);
