@@ -20,13 +20,15 @@
 //   KC: ds_read_b128, lane l -> row l%32, k chunk from l/32;
 //   KO bf16: ds_read_b64_tr_b16 (LDS transpose read), two per fragment;
 //   KO fp32: four ds_read_b32.
-// Eight waves (two per SIMD, 2 x 4 grid of 128 x 64 wave tiles by default),
-// so one wave's LDS or barrier wait is covered by the other's MFMAs.
-// NS = 4 LDS stages: the loads of tile k+3 are issued while tile k is
-// computed, so each load has three compute phases to land.  One barrier per
-// tile; the first fragments of the next tile are read right after it while
-// the last MFMAs of the current tile (operands already in registers) run.
-//
+// Eight waves (two per SIMD), one workgroup per CU, so one wave's LDS or
+// barrier wait is covered by the other's MFMAs.  NS LDS stages: the loads of
+// tile k+NS-1 are issued while tile k is computed.  One barrier per tile.
+// Fragment schedule (registers are the limit: a 256 x 384 block holds 192
+// fp32 accumulators per lane): B fragments are double-buffered across the
+// two k steps of a tile; each A fragment is re-read in place right after the
+// MFMAs of its row, so the next step's A is in flight while the remaining
+// rows run.  The barrier sits after the first MFMA row of the second step,
+// which gives the last A read of the first step time to land.
 // Matrix-core atom: 32x32 output.  bf16: v_mfma_f32_32x32x16_bf16 (8 k per
 // lane); fp32: four v_mfma_f32_32x32x2_f32 (one k per lane each).  A and B
 // fragments use the same per-lane k assignment (lane group h = l/32 holds k
@@ -87,7 +89,7 @@ template <> struct Elem<float> {
 // the raw-buffer format word.
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint64_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : static_cast<uint32_t>(bytes);
+  const uint32_t n = (bytes >> 31) != 0 ? 0x7FFFFFF0u : static_cast<uint32_t>(bytes);
   return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xFFFFu, n, 0x00020000u};
 }
 
@@ -136,13 +138,18 @@ struct StageLoader {
   static_assert(R * 64 % (1024 * NWAVES) == 0, "stage must split evenly over the waves");
   static_assert(KC || (CPR % 16 == 0), "k-outer tiles need >= 256 bytes per k row");
 
-  uint32_t voff[NI];   // byte offset from the tile's base (k part excluded for KC)
-  int rk[NI];          // KC: element offset of the chunk along k; KO: k row
-  bool ok[NI];         // row (KC) / column chunk (KO) inside the operand
+  // byte offset from the tile's base (k part excluded for KC); kOOB when the
+  // row (KC) / column chunk (KO) lies outside the operand.  kOOB plus any k
+  // offset stays past every record count.
+  uint32_t voff[NI];
 
   __device__ __forceinline__ static int fko(int k) {
     return SZ == 2 ? 4 * (k & 3) : 8 * ((k >> 2) & 1);
   }
+  // k-contiguous tiles: element offset along k of the lane's chunk (the same
+  // for every instruction).  k-outer tiles need no such check: their buffer
+  // record ends at row k_lim.
+  __device__ __forceinline__ static int rel_k(int lane) { return ((lane & 3) ^ ((lane >> 4) & 3)) * VEC; }
 
   __device__ __forceinline__ void init(const Operand<T>& op, int wave, int lane) {
 #pragma unroll
@@ -151,41 +158,37 @@ struct StageLoader {
       if (KC) {
         const int r = S >> 2, p = S & 3;
         const int c = p ^ ((r >> 2) & 3);
-        voff[i] = static_cast<uint32_t>(r * op.ld * SZ + c * 16);
-        rk[i] = c * VEC;
-        ok[i] = op.r0 + r < op.r_lim;
+        voff[i] = op.r0 + r < op.r_lim ? static_cast<uint32_t>(r * op.ld * SZ + c * 16) : kOOB;
       } else {
         const int k = S / CPR, p = S % CPR;
         const int c = p ^ fko(k);
-        voff[i] = static_cast<uint32_t>(k * op.ld * SZ + c * 16);
-        rk[i] = k;
-        ok[i] = op.r0 + c * VEC < op.r_lim;
+        voff[i] = op.r0 + c * VEC < op.r_lim ? static_cast<uint32_t>(k * op.ld * SZ + c * 16) : kOOB;
       }
     }
   }
 
-  // Buffer resource of the k tile starting at k0 (wave-uniform).
+  // Buffer resource of the k tile starting at k0 (wave-uniform).  For a
+  // k-outer tile the record stops at row k_lim, so rows past it read as zero.
   __device__ __forceinline__ u32x4 rsrc(const Operand<T>& op, int k0) const {
     if (KC) {
       const long base = static_cast<long>(op.r0) * op.ld;
       return make_rsrc(op.ptr + base, static_cast<uint64_t>(op.extent - base) * SZ);
     }
+    // rows [k0, k_lim) of the tile; extent >= k_lim * ld for every k-outer operand
+    if (k0 >= op.k_lim) return make_rsrc(op.ptr, 0);
     const long base = static_cast<long>(k0) * op.ld + op.r0;
-    return make_rsrc(op.ptr + base, static_cast<uint64_t>(op.extent - base) * SZ);
+    return make_rsrc(op.ptr + base, static_cast<uint64_t>(static_cast<long>(op.k_lim - k0) * op.ld - op.r0) * SZ);
   }
 
   // Issue instructions [I0, I1) of the k tile starting at k0 into LDS `dst`.
   template <int I0, int I1>
   __device__ __forceinline__ void issue(const Operand<T>& op, const u32x4& rs, int k0, char* dst,
                                         int wave) const {
+    const bool kc_ok = !KC || k0 + rel_k(threadIdx.x & 63) < op.k_lim;
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
-      uint32_t o;
-      if (KC)
-        o = (ok[i] && k0 + rk[i] < op.k_lim) ? voff[i] + static_cast<uint32_t>(k0 * SZ) : kOOB;
-      else
-        o = (ok[i] && k0 + rk[i] < op.k_lim) ? voff[i] : kOOB;
-      lds_dma16(rs, o, lds_addr(dst + (wave * NI + i) * 1024));
+      const uint32_t o = KC ? voff[i] + static_cast<uint32_t>(k0 * SZ) : voff[i];
+      lds_dma16(rs, kc_ok ? o : kOOB, lds_addr(dst + (wave * NI + i) * 1024));
     }
   }
   __device__ __forceinline__ void issue_all(const Operand<T>& op, int k0, char* dst, int wave) const {
@@ -232,7 +235,6 @@ struct Gemm {
   static constexpr int SZ = static_cast<int>(sizeof(T));
   static constexpr int BK = 64 / SZ;             // k per tile
   static constexpr int NS = NS_;                 // LDS stages
-  static constexpr bool EARLY = false;           // refill a stage right after the barrier that frees it
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NWAVES;         // two waves per SIMD by default
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -248,20 +250,16 @@ struct Gemm {
   using RB = FragReader<T, BN, B_KC>;
   static constexpr int NI = LA::NI + LB::NI;     // load instructions per wave per tile
 
-  struct Frags {
-    u32x4 a[FM], b[FN];
-  };
-  __device__ __forceinline__ static void read(Frags& f, const char* st, int kk, int wm, int wn, int lane) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) f.a[i] = RA::read(st, wm * WM + 32 * i, kk, lane);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) f.b[j] = RB::read(st + A_BYTES, wn * WN + 32 * j, kk, lane);
+  __device__ __forceinline__ static u32x4 read_a(const char* st, int kk, int wm, int i, int lane) {
+    return RA::read(st, wm * WM + 32 * i, kk, lane);
   }
-  __device__ __forceinline__ static void mma(f32x16 (&acc)[FM][FN], const Frags& f) {
+  __device__ __forceinline__ static void read_b(u32x4 (&b)[FN], const char* st, int kk, int wn, int lane) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) b[j] = RB::read(st + A_BYTES, wn * WN + 32 * j, kk, lane);
+  }
+  __device__ __forceinline__ static void mma_row(f32x16 (&acc)[FM][FN], int i, const u32x4& a, const u32x4 (&b)[FN]) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) Elem<T>::mma(acc[i][j], f.a[i], f.b[j]);
+    for (int j = 0; j < FN; ++j) Elem<T>::mma(acc[i][j], a, b[j]);
   }
   // wait until at most `tiles` tiles of this wave's loads are in flight
   __device__ __forceinline__ static void wait_tiles(int tiles) {
@@ -281,11 +279,12 @@ struct Gemm {
   // acc = sum over k in [k_begin, k_end) of A(m, k) B(n, k).  Leaves LDS free
   // (a barrier follows the last tile).
   //   prologue: tiles 0..NS-2 in flight, wait for tile 0, barrier, read the
-  //             fragments of tile 0 step 0;
-  //   tile kt:  issue tile kt+NS-1 into the stage tile kt-1 used; read step
-  //             1 fragments; MFMAs of step 0; wait for own loads of tile
-  //             kt+1; barrier; read step 0 fragments of tile kt+1; MFMAs of
-  //             step 1 of tile kt.
+  //             step-0 fragments of tile 0;
+  //   tile kt:  issue tile kt+NS-1 into the stage tile kt-1 used; read the
+  //             step-1 B fragments; per row i: MFMAs of step 0, re-read A[i]
+  //             for step 1; per row i: MFMAs of step 1 (after row 0: wait
+  //             for own loads of tile kt+1, barrier, read its step-0 B), re-
+  //             read A[i] for step 0 of tile kt+1.
   __device__ __forceinline__ static void run(const Operand<T>& A, const Operand<T>& B, int k_begin, int k_end,
                                              char* lds, f32x16 (&acc)[FM][FN]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -308,43 +307,52 @@ struct Gemm {
     LB lb;
     la.init(a, wave, lane);
     lb.init(b, wave, lane);
-    constexpr int PRO = EARLY ? NS : NS - 1;  // tiles in flight before the first MFMA
 #pragma unroll
-    for (int t = 0; t < PRO; ++t) {
+    for (int t = 0; t < NS - 1; ++t) {
       if (t < nk) {
         la.issue_all(a, k_begin + t * BK, lds + t * STAGE, wave);
         lb.issue_all(b, k_begin + t * BK, lds + t * STAGE + A_BYTES, wave);
       }
     }
-    wait_tiles(min(PRO - 1, nk - 1));
+    wait_tiles(min(NS - 2, nk - 1));
     lds_barrier();
-    Frags f0, f1;
-    read(f0, lds, 0, wm, wn, lane);
+    u32x4 af[FM], b0[FN], b1[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = read_a(lds, 0, wm, i, lane);
+    read_b(b0, lds, 0, wn, lane);
     for (int kt = 0; kt < nk; ++kt) {
       const char* cur = lds + (kt % NS) * STAGE;
-      if (!EARLY && kt + NS - 1 < nk) {
+      const char* nxt = lds + ((kt + 1) % NS) * STAGE;
+      const bool more = kt + 1 < nk;
+      if (kt + NS - 1 < nk) {
         char* dst = lds + ((kt + NS - 1) % NS) * STAGE;
         la.issue_all(a, k_begin + (kt + NS - 1) * BK, dst, wave);
         lb.issue_all(b, k_begin + (kt + NS - 1) * BK, dst + A_BYTES, wave);
       }
-      // The scheduling fences keep each step's fragment reads ahead of the
-      // MFMAs of the previous step (left alone, the scheduler sinks them
-      // next to their consumers and exposes the LDS latency every step).
-      read(f1, cur, 1, wm, wn, lane);
+      // The scheduling fences keep every fragment read where it is written:
+      // left alone, the scheduler sinks reads next to their consumers and
+      // exposes the LDS latency at every step.
+      read_b(b1, cur, 1, wn, lane);
       __builtin_amdgcn_sched_barrier(0);
-      mma(acc, f0);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_tiles(min(NS - 2, nk - kt - 2));  // tile kt+1 has landed (own loads)
-      lds_barrier();                          // tile kt+1 visible; stage of kt free
-      if (EARLY && kt + NS < nk) {
-        char* dst = lds + (kt % NS) * STAGE;
-        la.issue_all(a, k_begin + (kt + NS) * BK, dst, wave);
-        lb.issue_all(b, k_begin + (kt + NS) * BK, dst + A_BYTES, wave);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        mma_row(acc, i, af[i], b0);
+        __builtin_amdgcn_sched_barrier(0);
+        af[i] = read_a(cur, 1, wm, i, lane);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (kt + 1 < nk) read(f0, lds + ((kt + 1) % NS) * STAGE, 0, wm, wn, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(acc, f1);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        mma_row(acc, i, af[i], b1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i == 0) {
+          wait_tiles(min(NS - 2, nk - kt - 2));  // tile kt+1 has landed (own loads)
+          lds_barrier();                          // tile kt+1 visible; stage of kt free
+          if (more) read_b(b0, nxt, 0, wn, lane);
+        }
+        if (more) af[i] = read_a(nxt, 0, wm, i, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __syncthreads();
   }

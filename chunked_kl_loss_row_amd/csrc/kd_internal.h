@@ -10,9 +10,11 @@ namespace kd {
 
 // Tile shapes fixed at compile time (they also fix the workspace layout).
 constexpr int kProjBM = 256;   // chunk rows per projection tile
-constexpr int kProjBN = 256;   // vocabulary entries per projection tile
-constexpr int kGradBM = 256;   // output rows per dH / dW tile
-constexpr int kGradBN = 256;   // hidden columns per dH / dW tile
+constexpr int kProjBN = 384;   // vocabulary entries per projection tile
+constexpr int kDhBM = 256;     // chunk rows per dH tile
+constexpr int kDhBN = 384;     // hidden columns per dH tile
+constexpr int kDwBM = 384;     // vocabulary rows per dW tile
+constexpr int kDwBN = 256;     // hidden columns per dW tile
 constexpr int kMaxSplit = 16;  // largest split of the dH reduction over V
 
 // Everything one chunk's kernels need.  Input pointers are already offset

@@ -16,16 +16,19 @@
 
 namespace kd {
 
+// Block tiles: 256 x 384 (projection, dH) and 384 x 256 (dW), eight waves.
+// The projection keeps three LDS stages: its epilogue tables need the room.
 template <typename T>
-using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true>;
-static_assert(Gemm<uint16_t, kProjBM, kProjBN, true, true>::NT == Gemm<float, kProjBM, kProjBN, true, true>::NT,
+using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3>;
+template <typename T>
+using DhGemm = Gemm<T, kDhBM, kDhBN, true, false>;
+template <typename T>
+using DwGemm = Gemm<T, kDwBM, kDwBN, false, false>;
+static_assert(ProjGemm<uint16_t>::NT == ProjGemm<float>::NT && DhGemm<uint16_t>::NT == DhGemm<float>::NT &&
+                  DwGemm<uint16_t>::NT == DwGemm<float>::NT,
               "one block size per kernel for both dtypes");
-template <typename T>
-using DhGemm = Gemm<T, kGradBM, kGradBN, true, false>;
-template <typename T>
-using DwGemm = Gemm<T, kGradBM, kGradBN, false, false>;
 
-constexpr int kStageRows = 128;           // rows of the fp32 epilogue stage
+constexpr int kStageRows = 64;            // rows of the fp32 epilogue stage
 constexpr int kStagePitch = kProjBN + 8;  // floats per stage row (rows 4 apart hit other banks)
 constexpr int kStageBytes = kStageRows * kStagePitch * 4;
 template <class G>
@@ -475,34 +478,32 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
   const Operand<T> A{dz, ldz, static_cast<long>(rows) * ldz, mt * G::BM, ldz, rows};
   const Operand<T> B{Hc, d, static_cast<long>(rows) * d, nt * G::BN, d, rows};
   G::run(A, B, 0, rows, smem, acc);
-  // dW += acc, software pipelined over 32-row blocks: the reads of block
-  // i+1 are in flight while block i is added and written.  Rows past v fall
-  // outside the region; columns past d get kOOB.
+  // dW += acc, one 32 x 32 accumulator atom at a time, software pipelined:
+  // the reads of the next PF atoms are in flight while an atom is added and
+  // written.  Rows past v fall outside the region; columns past d get kOOB.
   const int row0 = mt * G::BM, col0 = nt * G::BN;
   const F32Region o(dW + static_cast<long>(row0) * d, static_cast<long>(v - row0) * d);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / (G::BN / G::WN), wn = wave % (G::BN / G::WN);
-  auto offset = [&](int i, int j, int e) -> uint32_t {
-    const int col = col0 + acc_col<G>(wn, j, lane);
-    return col < d ? static_cast<uint32_t>((acc_row<G>(wm, i, e, lane) * d + col) * 4) : kOOB;
+  auto offset = [&](int n, int e) -> uint32_t {
+    const int col = col0 + acc_col<G>(wn, n % G::FN, lane);
+    return col < d ? static_cast<uint32_t>((acc_row<G>(wm, n / G::FN, e, lane) * d + col) * 4) : kOOB;
   };
-  float old[2][G::FN][16];
+  constexpr int NA = G::FM * G::FN, PF = 1;
+  float old[PF + 1][16];
 #pragma unroll
-  for (int j = 0; j < G::FN; ++j)
+  for (int n = 0; n < PF && n < NA; ++n)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) old[0][j][e] = o.load(offset(0, j, e));
+    for (int e = 0; e < 16; ++e) old[n][e] = o.load(offset(n, e));
 #pragma unroll
-  for (int i = 0; i < G::FM; ++i) {
-    if (i + 1 < G::FM) {
+  for (int n = 0; n < NA; ++n) {
+    if (n + PF < NA) {
 #pragma unroll
-      for (int j = 0; j < G::FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) old[(i + 1) & 1][j][e] = o.load(offset(i + 1, j, e));
+      for (int e = 0; e < 16; ++e) old[(n + PF) % (PF + 1)][e] = o.load(offset(n + PF, e));
     }
 #pragma unroll
-    for (int j = 0; j < G::FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o.store(old[i & 1][j][e] + acc[i][j][e], offset(i, j, e));
+    for (int e = 0; e < 16; ++e)
+      o.store(old[n % (PF + 1)][e] + acc[n / G::FN][n % G::FN][e], offset(n, e));
   }
 }
 
@@ -513,7 +514,7 @@ int dh_split_for(int chunk, int d, int ldz, int* kslice) {
   // Split the V reduction so the grid fills the 256 compute units with
   // little tail: the smallest split whose last wave of workgroups is >= 90%
   // full, at least 8 k tiles per slice.
-  const int mt = (chunk + kGradBM - 1) / kGradBM, nt = (d + kGradBN - 1) / kGradBN;
+  const int mt = (chunk + kDhBM - 1) / kDhBM, nt = (d + kDhBN - 1) / kDhBN;
   const int tiles = mt * nt;
   const int bk = 64;  // k tile of the bf16 engine (the fp32 engine's 32 divides it)
   int best = 1;
@@ -580,7 +581,7 @@ void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStre
 }
 
 void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s) {
-  const int mtn = (a.rows + kGradBM - 1) / kGradBM, ntn = (a.d + kGradBN - 1) / kGradBN;
+  const int mtn = (a.rows + kDhBM - 1) / kDhBM, ntn = (a.d + kDhBN - 1) / kDhBN;
   const int split = a.dh_split;
   const dim3 grid(xcd_grid(mtn * ntn * split)), block(DhGemm<uint16_t>::NT);
   float* out = split == 1 ? dH : a.dhp;
@@ -604,7 +605,7 @@ void launch_dh_reduce(const ChunkArgs& a, float* dH, hipStream_t s) {
 }
 
 void launch_bwd_dw(const ChunkArgs& a, float* dW, hipStream_t s) {
-  const int mtn = (a.v + kGradBM - 1) / kGradBM, ntn = (a.d + kGradBN - 1) / kGradBN;
+  const int mtn = (a.v + kDwBM - 1) / kDwBM, ntn = (a.d + kDwBN - 1) / kDwBN;
   const dim3 grid(xcd_grid(mtn * ntn)), block(DwGemm<uint16_t>::NT);
   if (a.x_bf16)
     k_bwd_dw<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.dz), a.ldz,
