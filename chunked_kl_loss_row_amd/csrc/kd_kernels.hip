@@ -478,32 +478,49 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
   const Operand<T> A{dz, ldz, static_cast<long>(rows) * ldz, mt * G::BM, ldz, rows};
   const Operand<T> B{Hc, d, static_cast<long>(rows) * d, nt * G::BN, d, rows};
   G::run(A, B, 0, rows, smem, acc);
-  // dW += acc, one 32 x 32 accumulator atom at a time, software pipelined:
-  // the reads of the next PF atoms are in flight while an atom is added and
-  // written.  Rows past v fall outside the region; columns past d get kOOB.
+  // dW += acc through LDS, one 64-row slice at a time (atom row s of both
+  // wave rows): the slice's accumulators go to LDS, then each wave adds whole
+  // rows to dW with coalesced 16-byte reads and writes (a lane per 16 bytes,
+  // a wave per 256-column row).  The reads of slice s+1 are issued before
+  // slice s is added; two LDS slice buffers alternate.  Rows past v fall
+  // outside the region; columns past d (a multiple of 4) get kOOB.
+  static_assert(G::BM / G::WM == 2 && G::BN == 256 && G::NT == 512, "slice layout: 2 wave rows, 64 lanes x 16 B");
+  constexpr int PITCH = G::BN + 8;                 // floats per LDS row (rows 4 apart on other banks)
+  constexpr int SLICE = 64 * PITCH;                // floats per slice buffer
+  constexpr int CH = 64 / (G::NT / 64);            // rows (16-byte chunks) per thread per slice
+  static_assert(2 * SLICE * 4 <= G::LDS_BYTES, "two slice buffers must fit in LDS");
   const int row0 = mt * G::BM, col0 = nt * G::BN;
   const F32Region o(dW + static_cast<long>(row0) * d, static_cast<long>(v - row0) * d);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / (G::BN / G::WN), wn = wave % (G::BN / G::WN);
-  auto offset = [&](int n, int e) -> uint32_t {
-    const int col = col0 + acc_col<G>(wn, n % G::FN, lane);
-    return col < d ? static_cast<uint32_t>((acc_row<G>(wm, n / G::FN, e, lane) * d + col) * 4) : kOOB;
+  float* stage = reinterpret_cast<float*>(smem);
+  const bool col_ok = col0 + 4 * lane < d;
+  auto offset = [&](int s, int u) -> uint32_t {
+    const int lr = wave + (G::NT / 64) * u;  // slice row of this wave's u-th chunk
+    const int row = (lr >> 5) * G::WM + 32 * s + (lr & 31);
+    return col_ok ? static_cast<uint32_t>((row * d + col0 + 4 * lane) * 4) : kOOB;
   };
-  constexpr int NA = G::FM * G::FN, PF = 1;
-  float old[PF + 1][16];
+  f32x4 old[2][CH];
 #pragma unroll
-  for (int n = 0; n < PF && n < NA; ++n)
+  for (int u = 0; u < CH; ++u) old[0][u] = o.load4(offset(0, u));
 #pragma unroll
-    for (int e = 0; e < 16; ++e) old[n][e] = o.load(offset(n, e));
+  for (int s = 0; s < G::FM; ++s) {
+    float* buf = stage + (s & 1) * SLICE;
 #pragma unroll
-  for (int n = 0; n < NA; ++n) {
-    if (n + PF < NA) {
+    for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) old[(n + PF) % (PF + 1)][e] = o.load(offset(n + PF, e));
+      for (int e = 0; e < 16; ++e)
+        buf[(wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * PITCH + acc_col<G>(wn, j, lane)] = acc[s][j][e];
+    lds_barrier();
+    if (s + 1 < G::FM) {
+#pragma unroll
+      for (int u = 0; u < CH; ++u) old[(s + 1) & 1][u] = o.load4(offset(s + 1, u));
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      o.store(old[n % (PF + 1)][e] + acc[n / G::FN][n % G::FN][e], offset(n, e));
+    for (int u = 0; u < CH; ++u) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(buf + (wave + (G::NT / 64) * u) * PITCH + 4 * lane);
+      o.store4(x + old[s & 1][u], offset(s, u));
+    }
   }
 }
 
