@@ -29,6 +29,7 @@ static_assert(ProjGemm<uint16_t>::NT == ProjGemm<float>::NT && DhGemm<uint16_t>:
               "one block size per kernel for both dtypes");
 
 constexpr int kStageRows = 64;            // rows of the fp32 epilogue stage
+constexpr int kMaxHits = 4;               // teacher ids per (row, tile) kept in LDS; more take the slow path
 constexpr int kStagePitch = kProjBN + 8;  // floats per stage row (rows 4 apart hit other banks)
 constexpr int kStageBytes = kStageRows * kStagePitch * 4;
 template <class G>
@@ -177,6 +178,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
   using G = ProjGemm<T>;
   __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
+  __shared__ uint32_t s_hit[G::BM][kMaxHits];  // (column in tile << 8) | key slot
   const int rtn = (rows + G::BM - 1) / G::BM;
   const int t = xcd_tile(blockIdx.x, rtn * nvt);
   if (t < 0) return;
@@ -191,19 +193,24 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
     }
     s_lo[r] = lo;
     s_hi[r] = hi;
+    if (hi - lo <= kMaxHits)
+      for (int q = lo; q < hi; ++q)
+        s_hit[r][q - lo] = ((keys[static_cast<long>(gr) * K + q] >> 8) - vt * G::BN) << 8 | static_cast<uint32_t>(q);
   }
   f32x16 acc[G::FM][G::FN];
   const Operand<T> A{H, d, static_cast<long>(rows) * d, rt * G::BM, rows, d};
   const Operand<T> B{W, d, static_cast<long>(v) * d, vt * G::BN, v, d};
   G::run(A, B, 0, d, smem, acc);
 
+  // The epilogue's barriers order LDS only: the global writes of one stage
+  // pass stay in flight through the next.
   float* stage = reinterpret_cast<float*>(smem);
   const int ncols = min(G::BN, v - vt * G::BN);
   const int g16 = tid >> 4, l16 = tid & 15;
 #pragma unroll
   for (int h = 0; h < G::BM / kStageRows; ++h) {
     stage_half<G>(stage, acc, h);
-    __syncthreads();
+    lds_barrier();
     for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
       const int row = h * kStageRows + rr, grow = rt * G::BM + row;
       if (grow >= rows) break;
@@ -232,12 +239,19 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
         ps[static_cast<long>(grow) * nvt + vt] = sm;
       }
       const int lo = s_lo[row], hi = s_hi[row];
-      for (int j = lo + l16; j < hi; j += 16) {
-        const int col = static_cast<int>(keys[static_cast<long>(grow) * K + j] >> 8) - vt * G::BN;
-        zgs[static_cast<long>(grow) * K + j] = stage[rr * kStagePitch + col];
+      if (hi - lo <= kMaxHits) {
+        if (l16 < hi - lo) {
+          const uint32_t u = s_hit[row][l16];
+          zgs[static_cast<long>(grow) * K + (u & 0xFFu)] = stage[rr * kStagePitch + (u >> 8)];
+        }
+      } else {
+        for (int j = lo + l16; j < hi; j += 16) {
+          const int col = static_cast<int>(keys[static_cast<long>(grow) * K + j] >> 8) - vt * G::BN;
+          zgs[static_cast<long>(grow) * K + j] = stage[rr * kStagePitch + col];
+        }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -335,6 +349,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
   __shared__ int s_lo[G::BM], s_hi[G::BM];
   __shared__ float s_lse2[G::BM], s_coef[G::BM], s_gm[G::BM];
   __shared__ int s_live[G::BM];
+  __shared__ int s_hcol[G::BM][kMaxHits];  // column in tile of the row's teacher ids here
+  __shared__ float s_hp[G::BM][kMaxHits];  // their teacher probabilities
   const int rtn = (rows + G::BM - 1) / G::BM;
   const int t = xcd_tile(blockIdx.x, rtn * nvt);
   if (t < 0) return;
@@ -362,6 +378,12 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
     s_coef[r] = coef;
     s_gm[r] = gm;
     s_live[r] = live;
+    if (hi - lo <= kMaxHits)
+      for (int q = lo; q < hi; ++q) {
+        const long kq = static_cast<long>(gr) * K + q;
+        s_hcol[r][q - lo] = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
+        s_hp[r][q - lo] = psort[kq];
+      }
   }
   f32x16 acc[G::FM][G::FN];
   const Operand<T> A{H, d, static_cast<long>(rows) * d, rt * G::BM, rows, d};
@@ -373,7 +395,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
 #pragma unroll
   for (int h = 0; h < G::BM / kStageRows; ++h) {
     stage_half<G>(stage, acc, h);
-    __syncthreads();
+    lds_barrier();
     for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
       const int row = h * kStageRows + rr, grow = rt * G::BM + row;
       if (grow >= rows) break;
@@ -388,14 +410,26 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = coef * fast_exp2(fmaf(x[e], kLog2e, -lse2));
-        for (int q = lo; q < hi; ++q) {
-          const long kq = static_cast<long>(grow) * K + q;
-          const int c = static_cast<int>(keys[kq] >> 8) - vt * G::BN - c0;
-          if (static_cast<unsigned>(c) < 4u) {
-            const float sub = psort[kq];
+        if (hi - lo <= kMaxHits) {
+          for (int q = 0; q < hi - lo; ++q) {
+            const int c = s_hcol[row][q] - c0;
+            if (static_cast<unsigned>(c) < 4u) {
+              const float sub = s_hp[row][q];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (c == e) o[e] -= sub;
+              for (int e = 0; e < 4; ++e)
+                if (c == e) o[e] -= sub;
+            }
+          }
+        } else {
+          for (int q = lo; q < hi; ++q) {
+            const long kq = static_cast<long>(grow) * K + q;
+            const int c = static_cast<int>(keys[kq] >> 8) - vt * G::BN - c0;
+            if (static_cast<unsigned>(c) < 4u) {
+              const float sub = psort[kq];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (c == e) o[e] -= sub;
+            }
           }
         }
         const int gc = vt * G::BN + c0;
@@ -410,7 +444,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
