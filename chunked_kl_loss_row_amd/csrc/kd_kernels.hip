@@ -215,24 +215,26 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
       const int row = h * kStageRows + rr, grow = rt * G::BM + row;
       if (grow >= rows) break;
       f32x4 x[G::BN / 64];
+#pragma unroll
+      for (int j = 0; j < G::BN / 64; ++j) x[j] = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + j * 64 + l16 * 4);
+      if (ncols < G::BN) {  // columns past v take no part (exp2(-inf) = 0)
+#pragma unroll
+        for (int j = 0; j < G::BN / 64; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j * 64 + l16 * 4 + e >= ncols) x[j][e] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < G::BN / 64; ++j) {
-        const int c0 = j * 64 + l16 * 4;
-        x[j] = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + c0);
+      for (int j = 0; j < G::BN / 64; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (c0 + e < ncols) mx = fmaxf(mx, x[j][e]);
-      }
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, x[j][e]);
       mx = group16_max(mx);
       float sm = 0.f;
 #pragma unroll
-      for (int j = 0; j < G::BN / 64; ++j) {
-        const int c0 = j * 64 + l16 * 4;
+      for (int j = 0; j < G::BN / 64; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (c0 + e < ncols) sm += fast_exp2((x[j][e] - mx) * kLog2e);
-      }
+        for (int e = 0; e < 4; ++e) sm += fast_exp2((x[j][e] - mx) * kLog2e);
       sm = group16_sum(sm);
       if (l16 == 0) {
         pm[static_cast<long>(grow) * nvt + vt] = mx;
@@ -392,6 +394,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
 
   float* stage = reinterpret_cast<float*>(smem);
   const int g16 = tid >> 4, l16 = tid & 15;
+  const bool full_tile = (vt + 1) * G::BN <= v;
 #pragma unroll
   for (int h = 0; h < G::BM / kStageRows; ++h) {
     stage_half<G>(stage, acc, h);
@@ -400,47 +403,63 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
       const int row = h * kStageRows + rr, grow = rt * G::BM + row;
       if (grow >= rows) break;
       const float lse2 = s_lse2[row], coef = s_coef[row], gm = s_gm[row];
-      const int lo = s_lo[row], hi = s_hi[row];
-      const bool live = s_live[row] != 0;
+      const int lo = s_lo[row], n = s_hi[row] - lo;
       T* out = dz + static_cast<long>(grow) * ldz + vt * G::BN;
+      float o[G::BN / 64][4];
+      if (s_live[row] != 0) {
 #pragma unroll
-      for (int j = 0; j < G::BN / 64; ++j) {
-        const int c0 = j * 64 + l16 * 4;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + c0);
-        float o[4];
+        for (int jj = 0; jj < G::BN / 64; ++jj) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + jj * 64 + l16 * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = coef * fast_exp2(fmaf(x[e], kLog2e, -lse2));
-        if (hi - lo <= kMaxHits) {
-          for (int q = 0; q < hi - lo; ++q) {
-            const int c = s_hcol[row][q] - c0;
-            if (static_cast<unsigned>(c) < 4u) {
-              const float sub = s_hp[row][q];
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (c == e) o[e] -= sub;
-            }
-          }
-        } else {
-          for (int q = lo; q < hi; ++q) {
-            const long kq = static_cast<long>(grow) * K + q;
-            const int c = static_cast<int>(keys[kq] >> 8) - vt * G::BN - c0;
-            if (static_cast<unsigned>(c) < 4u) {
-              const float sub = psort[kq];
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (c == e) o[e] -= sub;
-            }
-          }
+          for (int e = 0; e < 4; ++e) o[jj][e] = coef * fast_exp2(fmaf(x[e], kLog2e, -lse2));
         }
-        const int gc = vt * G::BN + c0;
+        // p of the row's teacher ids in this tile, subtracted before the single
+        // rounding (c: column in the tile relative to this lane's first one)
+        for (int q = 0; q < n; ++q) {
+          int c;
+          float sub;
+          if (n <= kMaxHits) {
+            c = s_hcol[row][q];
+            sub = s_hp[row][q];
+          } else {
+            const long kq = static_cast<long>(grow) * K + lo + q;
+            c = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
+            sub = psort[kq];
+          }
+          c -= l16 * 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (live && gc + e < v) ? gm * o[e] : 0.f;
+          for (int jj = 0; jj < G::BN / 64; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[jj][e] -= (c == jj * 64 + e) ? sub : 0.f;
+        }
+#pragma unroll
+        for (int jj = 0; jj < G::BN / 64; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[jj][e] *= gm;
+        if (!full_tile) {  // columns past v: zero padding of dZ
+#pragma unroll
+          for (int jj = 0; jj < G::BN / 64; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (vt * G::BN + jj * 64 + l16 * 4 + e >= v) o[jj][e] = 0.f;
+        }
+      } else {  // masked row: exact zeros, whatever its inputs hold
+#pragma unroll
+        for (int jj = 0; jj < G::BN / 64; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[jj][e] = 0.f;
+      }
+#pragma unroll
+      for (int jj = 0; jj < G::BN / 64; ++jj) {
+        const int c0 = jj * 64 + l16 * 4;
         if constexpr (sizeof(T) == 2) {
-          uint32_t lo2 = static_cast<uint32_t>(Tr::from_f32(o[0])) | (static_cast<uint32_t>(Tr::from_f32(o[1])) << 16);
-          uint32_t hi2 = static_cast<uint32_t>(Tr::from_f32(o[2])) | (static_cast<uint32_t>(Tr::from_f32(o[3])) << 16);
+          const uint32_t lo2 = static_cast<uint32_t>(Tr::from_f32(o[jj][0])) |
+                               (static_cast<uint32_t>(Tr::from_f32(o[jj][1])) << 16);
+          const uint32_t hi2 = static_cast<uint32_t>(Tr::from_f32(o[jj][2])) |
+                               (static_cast<uint32_t>(Tr::from_f32(o[jj][3])) << 16);
           *reinterpret_cast<uint2*>(out + c0) = make_uint2(lo2, hi2);
         } else {
-          *reinterpret_cast<f32x4*>(out + c0) = f32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4*>(out + c0) = f32x4{o[jj][0], o[jj][1], o[jj][2], o[jj][3]};
         }
       }
     }
