@@ -73,6 +73,13 @@ template <> struct Elem<uint16_t> {  // bf16 as raw bits
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
 };
+// Two fp32 values rounded to bf16 (nearest even) and packed low, high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
 template <> struct Elem<float> {
   static constexpr int VEC = 4;
   __device__ __forceinline__ static float to_f32(float v) { return v; }

@@ -332,9 +332,9 @@ __global__ void k_zero_loss(float* loss) { loss[0] = 0.f; }
 // backward: recompute the projection and form the closed-form dZ
 // ---------------------------------------------------------------------------
 // dZ_iv = g m_i (s_i exp(z_iv - lse_i) - sum_k p_ik [t_ik = v]), evaluated in
-// fp32 in that order (the bracket first, then g) with the -p terms applied
-// before the single rounding to the storage dtype.  Columns in [v, ldz) are
-// written as zeros (padding of the row).
+// fp32 as (g s_i) exp(z_iv - lse_i) - g p_ik, the -g p terms applied before
+// the single rounding to the storage dtype.  Masked rows and columns in
+// [v, ldz) (padding of the row) are written as exact zeros.
 template <typename T>
 __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, const T* __restrict__ W,
                                                    int rows, int d, int v, int nvt, int K, int ldz,
@@ -346,7 +346,6 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ gptr, T* __restrict__ dz) {
   using G = ProjGemm<T>;
-  using Tr = Elem<T>;
   __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
   __shared__ float s_lse2[G::BM], s_coef[G::BM], s_gm[G::BM];
@@ -371,7 +370,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
         lo = lb[static_cast<long>(gr) * (nvt + 1) + vt];
         hi = lb[static_cast<long>(gr) * (nvt + 1) + vt + 1];
         gm = g;
-        coef = ssum[gr];
+        coef = g * ssum[gr];  // g folded into the row coefficient
       }
     }
     s_lo[r] = lo;
@@ -427,15 +426,12 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
             sub = psort[kq];
           }
           c -= l16 * 4;
+          sub *= gm;
 #pragma unroll
           for (int jj = 0; jj < G::BN / 64; ++jj)
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[jj][e] -= (c == jj * 64 + e) ? sub : 0.f;
         }
-#pragma unroll
-        for (int jj = 0; jj < G::BN / 64; ++jj)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[jj][e] *= gm;
         if (!full_tile) {  // columns past v: zero padding of dZ
 #pragma unroll
           for (int jj = 0; jj < G::BN / 64; ++jj)
@@ -452,12 +448,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
 #pragma unroll
       for (int jj = 0; jj < G::BN / 64; ++jj) {
         const int c0 = jj * 64 + l16 * 4;
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t lo2 = static_cast<uint32_t>(Tr::from_f32(o[jj][0])) |
-                               (static_cast<uint32_t>(Tr::from_f32(o[jj][1])) << 16);
-          const uint32_t hi2 = static_cast<uint32_t>(Tr::from_f32(o[jj][2])) |
-                               (static_cast<uint32_t>(Tr::from_f32(o[jj][3])) << 16);
-          *reinterpret_cast<uint2*>(out + c0) = make_uint2(lo2, hi2);
+        if constexpr (sizeof(T) == 2) {  // one nearest-even rounding per value, two per instruction
+          *reinterpret_cast<uint2*>(out + c0) = make_uint2(pack_bf16x2(o[jj][0], o[jj][1]), pack_bf16x2(o[jj][2], o[jj][3]));
         } else {
           *reinterpret_cast<f32x4*>(out + c0) = f32x4{o[jj][0], o[jj][1], o[jj][2], o[jj][3]};
         }

@@ -166,8 +166,8 @@ def test_g_scales_gradients():
     log("case g scaling")
     a = run_hip(d, 128, g=1.0)
     b = run_hip(d, 128, g=-2.5)
-    # g multiplies the fp32 bracket before the gradient GEMMs: linear up to
-    # the GEMMs' own rounding
+    # g scales the row coefficient and the teacher term in fp32 before the
+    # gradient GEMMs: linear up to fp32 rounding
     assert rel_fro(b["dH"].cpu().numpy(), -2.5 * a["dH"].cpu().numpy()) <= 1e-6
     assert rel_fro(b["dW"].cpu().numpy(), -2.5 * a["dW"].cpu().numpy()) <= 1e-6
     ref = oracle.run(inp, g=-2.5)
