@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt-oss-20b-32k")
     ap.add_argument("--chunk", type=int, default=None, help="override the workload's chunk size")
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=3072, help="rows of the CPU oracle sample (about 15-20 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
                     help="rocprofv3 FETCH_SIZE/WRITE_SIZE summary of the dominant kernel "
