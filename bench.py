@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--traffic", default=None,
                     help="rocprofv3 FETCH_SIZE/WRITE_SIZE summary of the dominant kernel "
                          "(default: profiles/kd_<kernel>_<workload>_traffic.txt)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip timing the single-call variant (kd_chunked_fwd_bwd)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy (y = -x, fp32) of this many MiB before warm-up: "
                          "the known-size dispatch that scales the memory counters of a --pmc run")
@@ -224,6 +226,39 @@ def main():
                     "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
                     "algorithmic_flop_per_launch": per_launch_flop, "avg_launch_ms": round(avg_s * 1e3, 4)}
 
+    variants = None
+    if not args.no_variants:
+        # kd_chunked_fwd_bwd: the forward keeps each chunk's fp32 logits and dZ is formed from
+        # them instead of recomputing the projection (6 N D V flops done; same results bit for bit)
+        del ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        wsf = torch.empty(B.kd_chunked_fwd_bwd_workspace_size(prob), dtype=torch.uint8, device="cuda")
+
+        def step_single():
+            B.kd_chunked_fwd_bwd(prob, H, W, ids, lg, mask, None, loss, lse, dH, dW, wsf, stream=stream)
+
+        vsteps = max(1, min(args.steps, 5))
+        step_single()
+        torch.cuda.synchronize()
+        B.kd_profile_enable(True)
+        v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        v0.record(stream)
+        for _ in range(vsteps):
+            step_single()
+        v1.record(stream)
+        torch.cuda.synchronize()
+        vms = v0.elapsed_time(v1) / vsteps
+        vk = B.kd_profile_all()
+        B.kd_profile_enable(False)
+        variants = {"single_call_cached_logits": {
+            "entry": "kd_chunked_fwd_bwd", "steps": vsteps, "ms_per_step": round(vms, 4),
+            "tokens_per_s": round(N / (vms * 1e-3), 1),
+            "tflops_done": round(6.0 * N * D * V / (vms * 1e-3) / 1e12, 2),
+            "peak_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 3),
+            "kernels": {k: round(t / n, 4) for k, (t, n) in vk.items() if n}}}
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] cpu oracle baseline on {args.cpu_rows} rows", file=sys.stderr, flush=True)
@@ -250,6 +285,7 @@ def main():
         "loss": loss_v,
         "roofline": roofline,
         "kernels": kernels,
+        "variants": variants,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

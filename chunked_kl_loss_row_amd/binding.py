@@ -20,8 +20,8 @@ KD_F32, KD_BF16 = 0, 1
 
 # names declared by include/kd_chunked.h and include/kd_profile.h
 EXPORTS = ("kd_chunked_workspace_size", "kd_status_string", "kd_chunked_fwd", "kd_chunked_bwd",
-           "kd_profile_enable", "kd_profile_read")
-KD_K_COUNT = 8
+           "kd_chunked_fwd_bwd_workspace_size", "kd_chunked_fwd_bwd", "kd_profile_enable", "kd_profile_read")
+KD_K_COUNT = 9
 
 
 class KDError(RuntimeError):
@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.kd_chunked_fwd.restype = ctypes.c_int
         L.kd_chunked_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.kd_chunked_bwd.restype = ctypes.c_int
+        L.kd_chunked_fwd_bwd_workspace_size.argtypes = [P]
+        L.kd_chunked_fwd_bwd_workspace_size.restype = ctypes.c_size_t
+        L.kd_chunked_fwd_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.kd_chunked_fwd_bwd.restype = ctypes.c_int
         L.kd_profile_enable.argtypes = [ctypes.c_int]
         L.kd_profile_enable.restype = ctypes.c_int
         L.kd_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -128,6 +132,23 @@ def kd_chunked_bwd(prob: KDProblem, H, W, t_ids, t_logits, mask, lse, grad_loss,
                               _ptr(workspace), wsb, _stream(stream))
     if check and st != KD_OK:
         raise KDError(st, "kd_chunked_bwd")
+    return st
+
+
+def kd_chunked_fwd_bwd_workspace_size(prob: KDProblem) -> int:
+    return int(lib().kd_chunked_fwd_bwd_workspace_size(ctypes.byref(prob)))
+
+
+def kd_chunked_fwd_bwd(prob: KDProblem, H, W, t_ids, t_logits, mask, grad_loss, loss, lse, dH, dW,
+                       workspace=None, workspace_bytes: Optional[int] = None, stream=None,
+                       check: bool = True) -> int:
+    """Enqueue forward + backward in one call (see include/kd_chunked.h)."""
+    wsb = _nbytes(workspace) if workspace_bytes is None else int(workspace_bytes)
+    st = lib().kd_chunked_fwd_bwd(ctypes.byref(prob), _ptr(H), _ptr(W), _ptr(t_ids), _ptr(t_logits),
+                                  _ptr(mask), _ptr(grad_loss), _ptr(loss), _ptr(lse), _ptr(dH), _ptr(dW),
+                                  _ptr(workspace), wsb, _stream(stream))
+    if check and st != KD_OK:
+        raise KDError(st, "kd_chunked_fwd_bwd")
     return st
 
 

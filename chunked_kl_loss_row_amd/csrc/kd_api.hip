@@ -32,11 +32,12 @@ bool dtype_ok(int t) { return t == KD_F32 || t == KD_BF16; }
 // Workspace regions, as byte offsets from the aligned base.
 struct Layout {
   int nvt, ldz, split, kslice;
-  size_t keys, psort, zgs, negent, ssum, lb, pm, ps, rl, loss_acc, dz, dhp;
+  size_t keys, psort, zgs, negent, ssum, lb, pm, ps, rl, loss_acc, dz, dhp, zc;
   size_t total;  // bytes from the aligned base
 };
 
-Layout layout_for(const kd_problem& p) {
+// `cached`: the single-call path also keeps the chunk's fp32 logits.
+Layout layout_for(const kd_problem& p, bool cached = false) {
   Layout L{};
   const size_t C = static_cast<size_t>(p.chunk), K = static_cast<size_t>(p.k);
   L.nvt = (p.v + kd::kProjBN - 1) / kd::kProjBN;
@@ -61,6 +62,7 @@ Layout layout_for(const kd_problem& p) {
   L.loss_acc = take(8);
   L.dz = take(C * static_cast<size_t>(L.ldz) * xs);
   L.dhp = take(L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
+  L.zc = take(cached ? C * static_cast<size_t>(L.ldz) * 4 : 0);
   L.total = o;
   return L;
 }
@@ -108,8 +110,8 @@ std::vector<ProfRec> g_prof_pending;
 std::vector<hipEvent_t> g_prof_pool;
 double g_prof_ms[KD_K_COUNT];
 int64_t g_prof_n[KD_K_COUNT];
-const char* const g_prof_names[KD_K_COUNT] = {"prep", "fwd_proj", "merge", "loss_fold",
-                                              "bwd_dz", "bwd_dh", "dh_reduce", "bwd_dw"};
+const char* const g_prof_names[KD_K_COUNT] = {"prep",   "fwd_proj", "merge",  "loss_fold", "bwd_dz",
+                                              "bwd_dh", "dh_reduce", "bwd_dw", "dz_cached"};
 
 hipEvent_t prof_event() {
   if (!g_prof_pool.empty()) {
@@ -151,7 +153,8 @@ void timed(int kind, hipStream_t s, F&& launch) {
 }
 
 ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const void* H, const void* W,
-                     const int32_t* ids, const void* logits, const uint8_t* mask, int64_t row0, int rows) {
+                     const int32_t* ids, const void* logits, const uint8_t* mask, int64_t row0, int rows,
+                     bool cached = false) {
   ChunkArgs a{};
   const size_t xs = p.x_dtype == KD_BF16 ? 2 : 4, ts = p.t_dtype == KD_BF16 ? 2 : 4;
   a.rows = rows;
@@ -181,6 +184,7 @@ ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const voi
   a.dhp = reinterpret_cast<float*>(base + L.dhp);
   a.dh_split = L.split;
   a.dh_kslice = L.kslice;
+  a.zc = cached ? reinterpret_cast<float*>(base + L.zc) : nullptr;
   return a;
 }
 
@@ -265,6 +269,49 @@ int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W, const i
     const ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows);
     timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
     timed(KD_K_BWD_DZ, s, [&] { kd::launch_bwd_dz(a, lse + row0, grad_loss, s); });
+    timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
+    if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
+    timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
+  }
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+size_t kd_chunked_fwd_bwd_workspace_size(const kd_problem* prob) {
+  if (check_problem(prob) != KD_OK) return 0;
+  return layout_for(*prob, true).total + kAlign;
+}
+
+int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, const int32_t* t_ids,
+                       const void* t_logits, const uint8_t* mask, const float* grad_loss, float* loss,
+                       float* lse, float* dH, float* dW, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int st = check_problem(prob);
+  if (st != KD_OK) return st;
+  const kd_problem& p = *prob;
+  if (!loss) return KD_ERR_NULL;
+  if (p.n > 0 && (!H || !W || !t_ids || !t_logits || !lse || !dH || !dW || !workspace)) return KD_ERR_NULL;
+  if (p.n > 0 && (!aligned16(H) || !aligned16(W) || !aligned16(dH))) return KD_ERR_ALIGN;
+  if (p.n > 0 && workspace_bytes < kd_chunked_fwd_bwd_workspace_size(prob)) return KD_ERR_WORKSPACE;
+  st = check_device();
+  if (st != KD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (p.n == 0) {
+    kd::launch_zero_loss(loss, s);
+    return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+  }
+  const Layout L = layout_for(p, true);
+  char* base = ws_base(workspace);
+  const int64_t nchunks = (p.n + p.chunk - 1) / p.chunk;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t row0 = c * p.chunk;
+    const int rows = static_cast<int>(p.n - row0 < p.chunk ? p.n - row0 : p.chunk);
+    const ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows, true);
+    timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
+    timed(KD_K_FWD_PROJ, s, [&] { kd::launch_fwd_proj(a, s); });
+    timed(KD_K_MERGE, s, [&] { kd::launch_merge(a, lse + row0, nullptr, nullptr, s); });
+    timed(KD_K_LOSS, s, [&] { kd::launch_loss_fold(a, c == 0, c == nchunks - 1, loss, s); });
+    timed(KD_K_DZ_CACHED, s, [&] { kd::launch_dz_cached(a, lse + row0, grad_loss, s); });
     timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
     if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
     timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });

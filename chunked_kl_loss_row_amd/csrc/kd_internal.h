@@ -44,6 +44,7 @@ struct ChunkArgs {
   double* loss_acc; // [1] running loss
   void* dz;         // [chunk][ldz] dZ in x dtype
   float* dhp;       // [split][chunk][d] split partials of dH
+  float* zc;        // [chunk][ldz] fp32 logits kept by the forward (single-call path), else null
   int dh_split;     // number of V slices of the dH reduction
   int dh_kslice;    // V entries per slice (multiple of the k tile)
 };
@@ -56,6 +57,7 @@ void launch_merge(const ChunkArgs& a, float* lse, float* row_loss, float* zg, hi
 void launch_loss_fold(const ChunkArgs& a, int first, int last, float* loss, hipStream_t s);
 void launch_zero_loss(float* loss, hipStream_t s);
 void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);
+void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);
 void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s);
 void launch_dh_reduce(const ChunkArgs& a, float* dH, hipStream_t s);
 void launch_bwd_dw(const ChunkArgs& a, float* dW, hipStream_t s);

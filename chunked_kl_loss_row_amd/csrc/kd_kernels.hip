@@ -144,6 +144,18 @@ __global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
 // helpers shared by the two projection epilogues
 // ---------------------------------------------------------------------------
 // Write the accumulators of the rows in stage half `h` to the fp32 stage.
+// dZ before the teacher term, (g s) exp(z - lse) with lse2 = lse log2(e), and
+// the teacher term's subtraction.  Contraction is off so that every kernel
+// forming dZ (recomputed or cached logits) rounds it the same way.
+__device__ __forceinline__ float dz_exp(float z, float coef, float lse2) {
+#pragma clang fp contract(off)
+  return coef * fast_exp2(fmaf(z, kLog2e, -lse2));
+}
+__device__ __forceinline__ float dz_sub(float o, float sub) {
+#pragma clang fp contract(off)
+  return o - sub;
+}
+
 template <typename G>
 __device__ __forceinline__ void stage_half(float* stage, const f32x16 (&acc)[G::FM][G::FN], int h) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -174,7 +186,8 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
                                                      const uint16_t* __restrict__ lb,
                                                      const uint32_t* __restrict__ keys,
                                                      float* __restrict__ zgs, float* __restrict__ pm,
-                                                     float* __restrict__ ps) {
+                                                     float* __restrict__ ps, float* __restrict__ zc,
+                                                     int ldz) {
   using G = ProjGemm<T>;
   __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
@@ -217,6 +230,11 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
       f32x4 x[G::BN / 64];
 #pragma unroll
       for (int j = 0; j < G::BN / 64; ++j) x[j] = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + j * 64 + l16 * 4);
+      if (zc) {  // single-call path: keep the fp32 logits of the chunk
+        float* zrow = zc + static_cast<long>(grow) * ldz + vt * G::BN + l16 * 4;
+#pragma unroll
+        for (int j = 0; j < G::BN / 64; ++j) *reinterpret_cast<f32x4*>(zrow + j * 64) = x[j];
+      }
       if (ncols < G::BN) {  // columns past v take no part (exp2(-inf) = 0)
 #pragma unroll
         for (int j = 0; j < G::BN / 64; ++j)
@@ -410,7 +428,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
         for (int jj = 0; jj < G::BN / 64; ++jj) {
           const f32x4 x = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + jj * 64 + l16 * 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[jj][e] = coef * fast_exp2(fmaf(x[e], kLog2e, -lse2));
+          for (int e = 0; e < 4; ++e) o[jj][e] = dz_exp(x[e], coef, lse2);
         }
         // p of the row's teacher ids in this tile, subtracted before the single
         // rounding (c: column in the tile relative to this lane's first one)
@@ -430,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
 #pragma unroll
           for (int jj = 0; jj < G::BN / 64; ++jj)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[jj][e] -= (c == jj * 64 + e) ? sub : 0.f;
+            for (int e = 0; e < 4; ++e) o[jj][e] = dz_sub(o[jj][e], (c == jj * 64 + e) ? sub : 0.f);
         }
         if (!full_tile) {  // columns past v: zero padding of dZ
 #pragma unroll
@@ -456,6 +474,67 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
       }
     }
     lds_barrier();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// single-call path: dZ from the logits the forward kept
+// ---------------------------------------------------------------------------
+// The same dZ as k_bwd_dz, bit for bit (same fp32 logits, same formula),
+// from the chunk's cached logits instead of a recomputed projection.  One
+// thread per 8 consecutive columns of a row (ldz is a multiple of the
+// projection tile width, so the 8 columns lie in one vocabulary tile).
+template <typename T>
+__global__ __launch_bounds__(256) void k_dz_cached(const float* __restrict__ zc, int ldz, int rows, int v,
+                                                   int K, int nvt, const uint16_t* __restrict__ lb,
+                                                   const uint32_t* __restrict__ keys,
+                                                   const float* __restrict__ psort,
+                                                   const float* __restrict__ ssum,
+                                                   const uint8_t* __restrict__ mask,
+                                                   const float* __restrict__ lse,
+                                                   const float* __restrict__ gptr, T* __restrict__ dz) {
+  const int per_row = ldz / 8;
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<long>(rows) * per_row) return;
+  const int row = static_cast<int>(idx / per_row), c0 = static_cast<int>(idx % per_row) * 8;
+  float o[8];
+  if (mask == nullptr || mask[row] != 0) {
+    const float g = gptr ? gptr[0] : 1.f;
+    const float lse2 = lse[row] * kLog2e, coef = g * ssum[row];
+    const f32x4 z0 = *reinterpret_cast<const f32x4*>(zc + static_cast<long>(row) * ldz + c0);
+    const f32x4 z1 = *reinterpret_cast<const f32x4*>(zc + static_cast<long>(row) * ldz + c0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = dz_exp(z0[e], coef, lse2);
+      o[e + 4] = dz_exp(z1[e], coef, lse2);
+    }
+    const int t = c0 / kProjBN;
+    const int lo = lb[static_cast<long>(row) * (nvt + 1) + t], hi = lb[static_cast<long>(row) * (nvt + 1) + t + 1];
+    for (int q = lo; q < hi; ++q) {
+      const long kq = static_cast<long>(row) * K + q;
+      const int c = static_cast<int>(keys[kq] >> 8) - c0;
+      if (static_cast<unsigned>(c) < 8u) {
+        const float sub = psort[kq] * g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = dz_sub(o[e], (c == e) ? sub : 0.f);
+      }
+    }
+    if (c0 + 8 > v) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c0 + e >= v) o[e] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  }
+  T* out = dz + static_cast<long>(row) * ldz + c0;
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint4*>(out) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+  } else {
+    *reinterpret_cast<f32x4*>(out) = f32x4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<f32x4*>(out + 4) = f32x4{o[4], o[5], o[6], o[7]};
   }
 }
 
@@ -609,11 +688,11 @@ void launch_fwd_proj(const ChunkArgs& a, hipStream_t s) {
   if (a.x_bf16)
     k_fwd_proj<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
                                                 static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v,
-                                                a.nvt, a.k, a.lb, a.keys, a.zgs, a.pm, a.ps);
+                                                a.nvt, a.k, a.lb, a.keys, a.zgs, a.pm, a.ps, a.zc, a.ldz);
   else
     k_fwd_proj<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
                                              a.rows, a.d, a.v, a.nvt, a.k, a.lb, a.keys, a.zgs, a.pm,
-                                             a.ps);
+                                             a.ps, a.zc, a.ldz);
 }
 
 void launch_merge(const ChunkArgs& a, float* lse, float* row_loss, float* zg, hipStream_t s) {
@@ -640,6 +719,17 @@ void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStre
     k_bwd_dz<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
                                            a.rows, a.d, a.v, a.nvt, a.k, a.ldz, a.lb, a.keys, a.psort,
                                            a.ssum, a.mask, lse, g, static_cast<float*>(a.dz));
+}
+
+void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s) {
+  const long threads = static_cast<long>(a.rows) * (a.ldz / 8);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256)), block(256);
+  if (a.x_bf16)
+    k_dz_cached<uint16_t><<<grid, block, 0, s>>>(a.zc, a.ldz, a.rows, a.v, a.k, a.nvt, a.lb, a.keys, a.psort,
+                                                 a.ssum, a.mask, lse, g, static_cast<uint16_t*>(a.dz));
+  else
+    k_dz_cached<float><<<grid, block, 0, s>>>(a.zc, a.ldz, a.rows, a.v, a.k, a.nvt, a.lb, a.keys, a.psort,
+                                              a.ssum, a.mask, lse, g, static_cast<float*>(a.dz));
 }
 
 void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s) {

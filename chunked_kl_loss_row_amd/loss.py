@@ -88,6 +88,26 @@ def backward(hidden, weight, t_ids, t_logits, mask, lse, grad_loss=None, dW=None
     return dH, dW
 
 
+def forward_backward(hidden, weight, t_ids, t_logits, mask=None, grad_loss=None, dW=None,
+                     chunk: int = 2048, workspace=None, dH=None) -> dict:
+    """kd_chunked_fwd_bwd: loss, lse, dH and dW (accumulated into ``dW`` when
+    given) in one call, each chunk's logits kept instead of recomputed.
+    Returns {"loss", "lse", "dH", "dW", "workspace"}."""
+    _check(hidden, weight, t_ids, t_logits, mask, grad_loss)
+    prob = make_problem(hidden, weight, t_ids, t_logits, chunk)
+    dev = hidden.device
+    ws = workspace if workspace is not None else torch.empty(B.kd_chunked_fwd_bwd_workspace_size(prob),
+                                                             dtype=torch.uint8, device=dev)
+    out = {"loss": torch.empty(1, dtype=torch.float32, device=dev),
+           "lse": torch.empty(prob.n, dtype=torch.float32, device=dev),
+           "dH": dH if dH is not None else torch.empty(prob.n, prob.d, dtype=torch.float32, device=dev),
+           "dW": dW if dW is not None else torch.zeros(prob.v, prob.d, dtype=torch.float32, device=dev),
+           "workspace": ws}
+    B.kd_chunked_fwd_bwd(prob, hidden, weight, t_ids, t_logits, mask, grad_loss, out["loss"], out["lse"],
+                         out["dH"], out["dW"], ws)
+    return out
+
+
 class KDChunkedKL(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, t_ids, t_logits, mask, chunk):

@@ -120,6 +120,34 @@ int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W,
                    const float* lse, const float* grad_loss, float* dH, float* dW,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace kd_chunked_fwd_bwd needs for `prob`: the fwd/bwd
+ * workspace plus one chunk of fp32 logits (chunk x 384*ceil(v/384) floats).
+ * Independent of n.  Returns 0 for an invalid problem. */
+size_t kd_chunked_fwd_bwd_workspace_size(const kd_problem* prob);
+
+/* Forward and backward in one call, for callers that know the upstream
+ * gradient g before the forward runs.  Same chunk walk and same results as
+ * kd_chunked_fwd followed by kd_chunked_bwd (loss, lse, dH and dW bit for
+ * bit), except that each chunk's fp32 logits are kept in the workspace by the
+ * forward projection and dZ is formed from them, instead of recomputing the
+ * projection: 6 n d v flops instead of 8, for one chunk of logits more
+ * workspace.  The pages' design recomputes, and note that the extra backward
+ * projection costs speed at short context (aihot.vn page "Tối ưu hóa chi phí
+ * chưng cất tri thức…", section "Điều này thay đổi những gì trong thực tế";
+ * agentlenshq.com page, section "パフォーマンスとメモリのベンチマーク").
+ *   H, W, t_ids, t_logits, mask   as for the forward
+ *   grad_loss [1]   float    device scalar g, NULL = 1
+ *   loss      [1]   float    out
+ *   lse       [n]   float    out
+ *   dH        [n,d] float    out, overwritten; masked rows are exactly zero
+ *   dW        [v,d] float    in/out, accumulated (+=)
+ *   workspace >= kd_chunked_fwd_bwd_workspace_size(prob) bytes
+ * Returns KD_OK or an error status (nothing enqueued on error). */
+int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W,
+                       const int32_t* t_ids, const void* t_logits, const uint8_t* mask,
+                       const float* grad_loss, float* loss, float* lse, float* dH, float* dW,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

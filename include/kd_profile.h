@@ -26,7 +26,8 @@ typedef enum kd_kernel_kind {
   KD_K_BWD_DH = 5,   /* dH = dZ W (split over V)                               */
   KD_K_DH_REDUCE = 6,/* fixed-order sum of the dH split partials               */
   KD_K_BWD_DW = 7,   /* dW += dZ^T H                                           */
-  KD_K_COUNT = 8
+  KD_K_DZ_CACHED = 8,/* single-call path: dZ from the forward's kept logits    */
+  KD_K_COUNT = 9
 } kd_kernel_kind;
 
 /* Turn event recording on (1) or off (0).  Either way the accumulated

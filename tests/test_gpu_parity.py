@@ -8,8 +8,8 @@ Tolerances (written here, applied element by element or per tensor):
   * gathered logits: bit-exact where the products are exact (integer-valued
     inputs); otherwise within fp32 accumulation error;
   * chunk size: lse and gathered logits bit-identical across chunk sizes.
-The shapes span several projection tiles (256 x 256) and gradient tiles
-(256 x 192) and end in ragged tails in every dimension.
+The shapes span several projection and dH tiles (256 x 384) and dW tiles
+(384 x 256) and end in ragged tails in every dimension.
 """
 import numpy as np
 import pytest
@@ -55,6 +55,7 @@ SMALL = [
     (300, 64, 520, 16, 300, "f32", "none"),
     (257, 200, 777, 256, 100, "bf16", "none"),
     (1024, 384, 5000, 100, 512, "f32", "random:100"),
+    (600, 520, 2000, 64, 256, "bf16", "random:40"),
 ]
 
 
