@@ -7,3 +7,4 @@ from .kd_oracle import (  # noqa: F401
     widen, teacher_distribution, student_logits, row_logsumexp,
     kd_forward, kd_backward, widen_inputs, run,
 )
+from .topk import teacher_topk  # noqa: F401
