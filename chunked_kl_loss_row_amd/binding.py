@@ -20,8 +20,9 @@ KD_F32, KD_BF16 = 0, 1
 
 # names declared by include/kd_chunked.h and include/kd_profile.h
 EXPORTS = ("kd_chunked_workspace_size", "kd_status_string", "kd_chunked_fwd", "kd_chunked_bwd",
-           "kd_chunked_fwd_bwd_workspace_size", "kd_chunked_fwd_bwd", "kd_profile_enable", "kd_profile_read")
-KD_K_COUNT = 9
+           "kd_chunked_fwd_bwd_workspace_size", "kd_chunked_fwd_bwd", "kd_teacher_topk_workspace_size",
+           "kd_teacher_topk", "kd_profile_enable", "kd_profile_read")
+KD_K_COUNT = 13
 
 
 class KDError(RuntimeError):
@@ -60,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.kd_chunked_fwd_bwd_workspace_size.restype = ctypes.c_size_t
         L.kd_chunked_fwd_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.kd_chunked_fwd_bwd.restype = ctypes.c_int
+        L.kd_teacher_topk_workspace_size.argtypes = [P]
+        L.kd_teacher_topk_workspace_size.restype = ctypes.c_size_t
+        L.kd_teacher_topk.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.kd_teacher_topk.restype = ctypes.c_int
         L.kd_profile_enable.argtypes = [ctypes.c_int]
         L.kd_profile_enable.restype = ctypes.c_int
         L.kd_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -149,6 +154,21 @@ def kd_chunked_fwd_bwd(prob: KDProblem, H, W, t_ids, t_logits, mask, grad_loss, 
                                   _ptr(workspace), wsb, _stream(stream))
     if check and st != KD_OK:
         raise KDError(st, "kd_chunked_fwd_bwd")
+    return st
+
+
+def kd_teacher_topk_workspace_size(prob: KDProblem) -> int:
+    return int(lib().kd_teacher_topk_workspace_size(ctypes.byref(prob)))
+
+
+def kd_teacher_topk(prob: KDProblem, H, W, ids, logits, overflow_rows=None, workspace=None,
+                    workspace_bytes: Optional[int] = None, stream=None, check: bool = True) -> int:
+    """Enqueue the teacher top-K producer (see include/kd_topk.h)."""
+    wsb = _nbytes(workspace) if workspace_bytes is None else int(workspace_bytes)
+    st = lib().kd_teacher_topk(ctypes.byref(prob), _ptr(H), _ptr(W), _ptr(ids), _ptr(logits), _ptr(overflow_rows),
+                               _ptr(workspace), wsb, _stream(stream))
+    if check and st != KD_OK:
+        raise KDError(st, "kd_teacher_topk")
     return st
 
 

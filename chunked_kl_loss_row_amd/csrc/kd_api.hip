@@ -18,6 +18,7 @@
 #include "kd_chunked.h"
 #include "kd_internal.h"
 #include "kd_profile.h"
+#include "kd_topk.h"
 
 namespace {
 
@@ -33,11 +34,16 @@ bool dtype_ok(int t) { return t == KD_F32 || t == KD_BF16; }
 struct Layout {
   int nvt, ldz, split, kslice;
   size_t keys, psort, zgs, negent, ssum, lb, pm, ps, rl, loss_acc, dz, dhp, zc;
+  size_t lmax, thr, cnt, cand;  // teacher top-K producer
   size_t total;  // bytes from the aligned base
 };
 
-// `cached`: the single-call path also keeps the chunk's fp32 logits.
-Layout layout_for(const kd_problem& p, bool cached = false) {
+enum class Mode { kLoss, kLossCached, kTopk };
+
+// kLossCached: the single-call path also keeps the chunk's fp32 logits;
+// kTopk: the teacher top-K producer (no dZ; per-row thresholds and
+// candidate lists instead).
+Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   Layout L{};
   const size_t C = static_cast<size_t>(p.chunk), K = static_cast<size_t>(p.k);
   L.nvt = (p.v + kd::kProjBN - 1) / kd::kProjBN;
@@ -60,9 +66,14 @@ Layout layout_for(const kd_problem& p, bool cached = false) {
   L.ps = take(C * L.nvt * 4);
   L.rl = take(C * 8);
   L.loss_acc = take(8);
-  L.dz = take(C * static_cast<size_t>(L.ldz) * xs);
-  L.dhp = take(L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
-  L.zc = take(cached ? C * static_cast<size_t>(L.ldz) * 4 : 0);
+  const bool loss = mode != Mode::kTopk;
+  L.dz = take(loss ? C * static_cast<size_t>(L.ldz) * xs : 0);
+  L.dhp = take(loss && L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
+  L.zc = take(mode == Mode::kLossCached ? C * static_cast<size_t>(L.ldz) * 4 : 0);
+  L.lmax = take(loss ? 0 : C * static_cast<size_t>(L.nvt) * kd::kTopkLanes * 4);
+  L.thr = take(loss ? 0 : C * 4);
+  L.cnt = take(loss ? 0 : C * 4);
+  L.cand = take(loss ? 0 : C * static_cast<size_t>(kd::kTopkCap) * 8);
   L.total = o;
   return L;
 }
@@ -110,8 +121,10 @@ std::vector<ProfRec> g_prof_pending;
 std::vector<hipEvent_t> g_prof_pool;
 double g_prof_ms[KD_K_COUNT];
 int64_t g_prof_n[KD_K_COUNT];
-const char* const g_prof_names[KD_K_COUNT] = {"prep",   "fwd_proj", "merge",  "loss_fold", "bwd_dz",
-                                              "bwd_dh", "dh_reduce", "bwd_dw", "dz_cached"};
+const char* const g_prof_names[KD_K_COUNT] = {"prep",      "fwd_proj",       "merge",         "loss_fold",
+                                              "bwd_dz",    "bwd_dh",         "dh_reduce",     "bwd_dw",
+                                              "dz_cached", "topk_maxima",    "topk_threshold", "topk_collect",
+                                              "topk_select"};
 
 hipEvent_t prof_event() {
   if (!g_prof_pool.empty()) {
@@ -278,7 +291,7 @@ int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W, const i
 
 size_t kd_chunked_fwd_bwd_workspace_size(const kd_problem* prob) {
   if (check_problem(prob) != KD_OK) return 0;
-  return layout_for(*prob, true).total + kAlign;
+  return layout_for(*prob, Mode::kLossCached).total + kAlign;
 }
 
 int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, const int32_t* t_ids,
@@ -300,7 +313,7 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, con
     kd::launch_zero_loss(loss, s);
     return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
   }
-  const Layout L = layout_for(p, true);
+  const Layout L = layout_for(p, Mode::kLossCached);
   char* base = ws_base(workspace);
   const int64_t nchunks = (p.n + p.chunk - 1) / p.chunk;
   for (int64_t c = 0; c < nchunks; ++c) {
@@ -315,6 +328,48 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, con
     timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
     if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
     timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
+  }
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+size_t kd_teacher_topk_workspace_size(const kd_problem* prob) {
+  if (check_problem(prob) != KD_OK) return 0;
+  return layout_for(*prob, Mode::kTopk).total + kAlign;
+}
+
+int kd_teacher_topk(const kd_problem* prob, const void* H, const void* W, int32_t* ids, float* logits,
+                    int* overflow_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_problem(prob);
+  if (st != KD_OK) return st;
+  const kd_problem& p = *prob;
+  if (p.n > 0 && (!H || !W || !ids || !logits || !workspace)) return KD_ERR_NULL;
+  if (p.n > 0 && (!aligned16(H) || !aligned16(W))) return KD_ERR_ALIGN;
+  if (p.n > 0 && workspace_bytes < kd_teacher_topk_workspace_size(prob)) return KD_ERR_WORKSPACE;
+  st = check_device();
+  if (st != KD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (overflow_rows) kd::launch_fill_u32(reinterpret_cast<uint32_t*>(overflow_rows), 1, 0u, s);
+  if (p.n == 0) return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+  const Layout L = layout_for(p, Mode::kTopk);
+  char* base = ws_base(workspace);
+  uint32_t* lmax = reinterpret_cast<uint32_t*>(base + L.lmax);
+  uint32_t* thr = reinterpret_cast<uint32_t*>(base + L.thr);
+  int* cnt = reinterpret_cast<int*>(base + L.cnt);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(base + L.cand);
+  const int64_t nchunks = (p.n + p.chunk - 1) / p.chunk;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t row0 = c * p.chunk;
+    const int rows = static_cast<int>(p.n - row0 < p.chunk ? p.n - row0 : p.chunk);
+    ChunkArgs a = chunk_args(p, L, base, H, W, nullptr, nullptr, nullptr, 0, rows);
+    const size_t xs = p.x_dtype == KD_BF16 ? 2 : 4;
+    a.H = static_cast<const char*>(H) + static_cast<size_t>(row0) * p.d * xs;
+    timed(KD_K_TOPK_MAXIMA, s, [&] { kd::launch_topk_maxima(a, lmax, s); });
+    timed(KD_K_TOPK_THRESHOLD, s, [&] { kd::launch_topk_threshold(a, lmax, thr, cnt, s); });
+    timed(KD_K_TOPK_COLLECT, s, [&] { kd::launch_topk_collect(a, thr, cnt, cand, s); });
+    timed(KD_K_TOPK_SELECT, s, [&] {
+      kd::launch_topk_select(a, cnt, cand, ids + row0 * p.k, logits + row0 * p.k, overflow_rows, s);
+    });
   }
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }

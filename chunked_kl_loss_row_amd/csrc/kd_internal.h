@@ -16,6 +16,8 @@ constexpr int kDhBN = 384;     // hidden columns per dH tile
 constexpr int kDwBM = 384;     // vocabulary rows per dW tile
 constexpr int kDwBN = 256;     // hidden columns per dW tile
 constexpr int kMaxSplit = 16;  // largest split of the dH reduction over V
+constexpr int kTopkCap = 8192; // candidate keys kept per row by the teacher top-K producer
+constexpr int kTopkLanes = 16; // sampled maxima per row and projection tile (one per epilogue lane)
 
 // Everything one chunk's kernels need.  Input pointers are already offset
 // to the chunk's first row; workspace pointers are chunk-local.
@@ -59,6 +61,12 @@ void launch_zero_loss(float* loss, hipStream_t s);
 void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);
 void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);
 void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s);
+void launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s);
+void launch_topk_maxima(const ChunkArgs& a, uint32_t* lmax, hipStream_t s);
+void launch_topk_threshold(const ChunkArgs& a, const uint32_t* lmax, uint32_t* thr, int* cnt, hipStream_t s);
+void launch_topk_collect(const ChunkArgs& a, const uint32_t* thr, int* cnt, uint64_t* cand, hipStream_t s);
+void launch_topk_select(const ChunkArgs& a, const int* cnt, const uint64_t* cand, int32_t* ids, float* logits,
+                        int* overflow, hipStream_t s);
 void launch_dh_reduce(const ChunkArgs& a, float* dH, hipStream_t s);
 void launch_bwd_dw(const ChunkArgs& a, float* dW, hipStream_t s);
 

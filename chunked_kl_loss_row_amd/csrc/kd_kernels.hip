@@ -649,6 +649,182 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
 }
 
 // ---------------------------------------------------------------------------
+// teacher top-K producer: the K largest logits of every row, largest first,
+// equal logits by the lower id, without the rows x vocabulary grid
+// ---------------------------------------------------------------------------
+// Keys: (ordered_key(z) << 32) | (0xFFFFFFFF - id) -- a larger key is a larger
+// logit, or the same logit with a lower id; keys of one row are distinct.
+//
+// Pass 1 records, per row and tile, each lane's largest key (16 lanes per
+// row, each over 24 of the tile's columns): kTopkLanes x nvt sampled maxima.
+// Threshold per row: the K-th largest of them.  They are keys of K distinct
+// logits of the row, so at least K logits are at or above it: every logit of
+// the top K is.  Rows with fewer than K sampled maxima take threshold 0 (every
+// logit; then v < 24 K <= 6144 <= kTopkCap).
+__global__ __launch_bounds__(256) void k_topk_threshold(const uint32_t* __restrict__ lmax, int nmax, int rows,
+                                                        int K, uint32_t* __restrict__ thr,
+                                                        int* __restrict__ cnt) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + w;
+  if (row >= rows) return;
+  uint32_t res = 0;
+  if (nmax >= K) {
+    const uint32_t* r = lmax + static_cast<long>(row) * nmax;
+    // MSB first: the largest res with #{maxima >= res} >= K
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t trial = res | (1u << b);
+      int c = 0;
+      for (int t = lane; t < nmax; t += 64) c += r[t] >= trial ? 1 : 0;
+      if (wave_sum(c) >= K) res = trial;
+    }
+  }
+  if (lane == 0) {
+    thr[row] = res;
+    cnt[row] = 0;
+  }
+}
+
+// Projection tile as in the forward.  PASS 0: the epilogue writes each lane's
+// largest key (padding columns excluded) to lmax.  PASS 1: it appends every
+// logit whose key is at or above its row's threshold to the row's candidate
+// list (one atomic add per row and tile with candidates; a list longer than
+// kTopkCap keeps kTopkCap entries and the select pass reports the row).
+template <typename T, int PASS>
+__global__ __launch_bounds__(512, 1) void k_topk_pass(const T* __restrict__ H, const T* __restrict__ W, int rows,
+                                                      int d, int v, int nvt, uint32_t* __restrict__ lmax,
+                                                      const uint32_t* __restrict__ thr, int* __restrict__ cnt,
+                                                      uint64_t* __restrict__ cand) {
+  using G = ProjGemm<T>;
+  __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
+  __shared__ uint32_t s_thr[G::BM];
+  const int rtn = (rows + G::BM - 1) / G::BM;
+  const int t = xcd_tile(blockIdx.x, rtn * nvt);
+  if (t < 0) return;
+  const int vt = t / rtn, rt = t % rtn;
+  const int tid = threadIdx.x;
+  if (PASS == 1)
+    for (int r = tid; r < G::BM; r += G::NT) {
+      const int gr = rt * G::BM + r;
+      s_thr[r] = gr < rows ? thr[gr] : 0xFFFFFFFFu;
+    }
+  f32x16 acc[G::FM][G::FN];
+  const Operand<T> A{H, d, static_cast<long>(rows) * d, rt * G::BM, rows, d};
+  const Operand<T> B{W, d, static_cast<long>(v) * d, vt * G::BN, v, d};
+  G::run(A, B, 0, d, smem, acc);
+
+  float* stage = reinterpret_cast<float*>(smem);
+  const int ncols = min(G::BN, v - vt * G::BN);
+  const int g16 = tid >> 4, l16 = tid & 15;
+#pragma unroll
+  for (int h = 0; h < G::BM / kStageRows; ++h) {
+    stage_half<G>(stage, acc, h);
+    lds_barrier();
+    for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
+      const int row = h * kStageRows + rr, grow = rt * G::BM + row;
+      if (grow >= rows) break;
+      const float* srow = stage + rr * kStagePitch + l16 * 4;
+      if (PASS == 0) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < G::BN / 64; ++j) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(srow + j * 64);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j * 64 + l16 * 4 + e < ncols) m = max(m, ordered_key(x[e]));
+        }
+        lmax[static_cast<long>(grow) * nvt * kTopkLanes + vt * kTopkLanes + l16] = m;  // 0: no column here
+        continue;
+      }
+      const uint32_t th = s_thr[row];
+      int nh = 0;
+#pragma unroll
+      for (int j = 0; j < G::BN / 64; ++j) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(srow + j * 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nh += (j * 64 + l16 * 4 + e < ncols && ordered_key(x[e]) >= th) ? 1 : 0;
+      }
+      const int total = static_cast<int>(group16_sum(static_cast<float>(nh)));
+      if (total > 0) {  // rare: the row's top-K region
+        int incl = nh;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const int y = __shfl_up(incl, o, 16);
+          if (l16 >= o) incl += y;
+        }
+        int base = 0;
+        if (l16 == 0) base = atomicAdd(cnt + grow, total);
+        base = __shfl(base, 0, 16) + incl - nh;
+        uint64_t* out = cand + static_cast<long>(grow) * kTopkCap;
+        for (int j = 0; j < G::BN / 64 && nh > 0; ++j) {
+          for (int e = 0; e < 4; ++e) {
+            const int col = j * 64 + l16 * 4 + e;
+            const uint32_t key = ordered_key(srow[j * 64 + e]);
+            if (col < ncols && key >= th) {
+              if (base < kTopkCap)
+                out[base] = (static_cast<uint64_t>(key) << 32) |
+                            static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(vt * G::BN + col));
+              ++base;
+              --nh;
+            }
+          }
+        }
+      }
+    }
+    lds_barrier();
+  }
+}
+
+// One workgroup per row: sort the row's candidate keys (bitonic, in LDS,
+// descending) and write the first K.  A row with more than kTopkCap
+// candidates is counted in *overflow (its record is then the best K of the
+// kept ones, not necessarily the exact top K).
+__global__ __launch_bounds__(256) void k_topk_select(const int* __restrict__ cnt,
+                                                     const uint64_t* __restrict__ cand, int K,
+                                                     int32_t* __restrict__ ids, float* __restrict__ logits,
+                                                     int* __restrict__ overflow) {
+  __shared__ uint64_t s[kTopkCap];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int c = cnt[row];
+  const int m = c < kTopkCap ? c : kTopkCap;
+  if (c > kTopkCap && tid == 0 && overflow) atomicAdd(overflow, 1);
+  int P = 1;
+  while (P < m) P <<= 1;
+  const uint64_t* src = cand + static_cast<long>(row) * kTopkCap;
+  for (int i = tid; i < P; i += 256) s[i] = i < m ? src[i] : 0ull;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P / 2; i += 256) {
+        const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+        const bool desc = (lo & size) == 0;  // blocks alternate; the final merge is descending
+        const uint64_t a = s[lo], b = s[hi];
+        if ((a < b) == desc) {
+          s[lo] = b;
+          s[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int j = tid; j < K; j += 256) {
+    const long o = static_cast<long>(row) * K + j;
+    if (j < m) {
+      const uint64_t key = s[j];
+      ids[o] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+      logits[o] = key_value(static_cast<uint32_t>(key >> 32));
+    } else {
+      ids[o] = -1;
+      logits[o] = -INFINITY;
+    }
+  }
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, size_t words, uint32_t value) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < words) p[i] = value;
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 int dh_split_for(int chunk, int d, int ldz, int* kslice) {
@@ -730,6 +906,44 @@ void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipS
   else
     k_dz_cached<float><<<grid, block, 0, s>>>(a.zc, a.ldz, a.rows, a.v, a.k, a.nvt, a.lb, a.keys, a.psort,
                                               a.ssum, a.mask, lse, g, static_cast<float*>(a.dz));
+}
+
+void launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s) {
+  if (words == 0) return;
+  k_fill_u32<<<dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, s>>>(p, words, value);
+}
+
+void launch_topk_maxima(const ChunkArgs& a, uint32_t* lmax, hipStream_t s) {
+  const int rtn = (a.rows + kProjBM - 1) / kProjBM;
+  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
+  if (a.x_bf16)
+    k_topk_pass<uint16_t, 0><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
+                                                    static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
+                                                    lmax, nullptr, nullptr, nullptr);
+  else
+    k_topk_pass<float, 0><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
+                                                 a.rows, a.d, a.v, a.nvt, lmax, nullptr, nullptr, nullptr);
+}
+
+void launch_topk_threshold(const ChunkArgs& a, const uint32_t* lmax, uint32_t* thr, int* cnt, hipStream_t s) {
+  k_topk_threshold<<<dim3((a.rows + 3) / 4), dim3(256), 0, s>>>(lmax, a.nvt * kTopkLanes, a.rows, a.k, thr, cnt);
+}
+
+void launch_topk_collect(const ChunkArgs& a, const uint32_t* thr, int* cnt, uint64_t* cand, hipStream_t s) {
+  const int rtn = (a.rows + kProjBM - 1) / kProjBM;
+  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
+  if (a.x_bf16)
+    k_topk_pass<uint16_t, 1><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
+                                                    static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
+                                                    nullptr, thr, cnt, cand);
+  else
+    k_topk_pass<float, 1><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
+                                                 a.rows, a.d, a.v, a.nvt, nullptr, thr, cnt, cand);
+}
+
+void launch_topk_select(const ChunkArgs& a, const int* cnt, const uint64_t* cand, int32_t* ids, float* logits,
+                        int* overflow, hipStream_t s) {
+  k_topk_select<<<dim3(a.rows), dim3(256), 0, s>>>(cnt, cand, a.k, ids, logits, overflow);
 }
 
 void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s) {

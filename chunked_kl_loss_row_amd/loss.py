@@ -108,6 +108,26 @@ def forward_backward(hidden, weight, t_ids, t_logits, mask=None, grad_loss=None,
     return out
 
 
+def teacher_topk(hidden, weight, k: int = 100, chunk: int = 2048, workspace=None) -> dict:
+    """kd_teacher_topk: the K largest logits of ``hidden @ weight.T`` per row
+    (ids int32, fp32 logits, largest first, ties by the lower id).  Returns
+    {"ids", "logits", "overflow_rows" (device int), "workspace"}."""
+    _check(hidden, weight)
+    n, d = hidden.shape
+    v = weight.shape[0]
+    if weight.shape[1] != d or hidden.dtype != weight.dtype:
+        raise ValueError("hidden [n,d] and weight [v,d] of one dtype")
+    prob = B.problem(n, d, v, k, chunk, _xdtype(hidden))
+    dev = hidden.device
+    ws = workspace if workspace is not None else torch.empty(B.kd_teacher_topk_workspace_size(prob),
+                                                             dtype=torch.uint8, device=dev)
+    out = {"ids": torch.empty(n, k, dtype=torch.int32, device=dev),
+           "logits": torch.empty(n, k, dtype=torch.float32, device=dev),
+           "overflow_rows": torch.zeros(1, dtype=torch.int32, device=dev), "workspace": ws}
+    B.kd_teacher_topk(prob, hidden, weight, out["ids"], out["logits"], out["overflow_rows"], ws)
+    return out
+
+
 class KDChunkedKL(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, t_ids, t_logits, mask, chunk):

@@ -27,7 +27,11 @@ typedef enum kd_kernel_kind {
   KD_K_DH_REDUCE = 6,/* fixed-order sum of the dH split partials               */
   KD_K_BWD_DW = 7,   /* dW += dZ^T H                                           */
   KD_K_DZ_CACHED = 8,/* single-call path: dZ from the forward's kept logits    */
-  KD_K_COUNT = 9
+  KD_K_TOPK_MAXIMA = 9,     /* top-K producer: projection + sampled row maxima   */
+  KD_K_TOPK_THRESHOLD = 10, /* top-K producer: per-row threshold                 */
+  KD_K_TOPK_COLLECT = 11,   /* top-K producer: projection + candidate collection */
+  KD_K_TOPK_SELECT = 12,    /* top-K producer: per-row sort of the candidates     */
+  KD_K_COUNT = 13
 } kd_kernel_kind;
 
 /* Turn event recording on (1) or off (0).  Either way the accumulated
