@@ -259,6 +259,39 @@ def main():
             "peak_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 3),
             "kernels": {k: round(t / n, 4) for k, (t, n) in vk.items() if n}}}
 
+        # kd_teacher_topk on the same shapes (H, W standing in for a teacher): the K largest
+        # logits per row, two projection passes (4 N D V flops done)
+        del wsf
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        tprob = B.problem(N, D, V, wl.k, chunk, B.KD_BF16 if wl.x_dtype == "bf16" else B.KD_F32)
+        wst = torch.empty(B.kd_teacher_topk_workspace_size(tprob), dtype=torch.uint8, device="cuda")
+        tids = torch.empty(N, wl.k, dtype=torch.int32, device="cuda")
+        tlog = torch.empty(N, wl.k, dtype=torch.float32, device="cuda")
+        ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+        def step_topk():
+            B.kd_teacher_topk(tprob, H, W, tids, tlog, ovf, wst, stream=stream)
+
+        step_topk()
+        torch.cuda.synchronize()
+        B.kd_profile_enable(True)
+        v0.record(stream)
+        for _ in range(vsteps):
+            step_topk()
+        v1.record(stream)
+        torch.cuda.synchronize()
+        tms = v0.elapsed_time(v1) / vsteps
+        tk = B.kd_profile_all()
+        B.kd_profile_enable(False)
+        variants["teacher_topk_producer"] = {
+            "entry": "kd_teacher_topk", "k": wl.k, "steps": vsteps, "ms_per_pass": round(tms, 4),
+            "tokens_per_s": round(N / (tms * 1e-3), 1),
+            "tflops_done": round(4.0 * N * D * V / (tms * 1e-3) / 1e12, 2),
+            "overflow_rows": int(ovf.item()),
+            "kernels": {k: round(t / n, 4) for k, (t, n) in tk.items() if n}}
+        del wst
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] cpu oracle baseline on {args.cpu_rows} rows", file=sys.stderr, flush=True)

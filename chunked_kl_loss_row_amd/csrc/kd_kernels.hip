@@ -661,24 +661,33 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
 // logits of the row, so at least K logits are at or above it: every logit of
 // the top K is.  Rows with fewer than K sampled maxima take threshold 0 (every
 // logit; then v < 24 K <= 6144 <= kTopkCap).
-__global__ __launch_bounds__(256) void k_topk_threshold(const uint32_t* __restrict__ lmax, int nmax, int rows,
-                                                        int K, uint32_t* __restrict__ thr,
-                                                        int* __restrict__ cnt) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + w;
-  if (row >= rows) return;
+// One workgroup per row; the row's maxima are staged in LDS when they fit.
+__global__ __launch_bounds__(256) void k_topk_threshold(const uint32_t* __restrict__ lmax, int nmax, int K,
+                                                        uint32_t* __restrict__ thr, int* __restrict__ cnt) {
+  constexpr int kLdsKeys = 16384;
+  __shared__ uint32_t s_v[kLdsKeys];
+  __shared__ int s_c[2][4];
+  const int row = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const uint32_t* r = lmax + static_cast<long>(row) * nmax;
   uint32_t res = 0;
   if (nmax >= K) {
-    const uint32_t* r = lmax + static_cast<long>(row) * nmax;
+    const bool staged = nmax <= kLdsKeys;
+    if (staged) {
+      for (int i = tid; i < nmax; i += 256) s_v[i] = r[i];
+      __syncthreads();
+    }
     // MSB first: the largest res with #{maxima >= res} >= K
     for (int b = 31; b >= 0; --b) {
       const uint32_t trial = res | (1u << b);
       int c = 0;
-      for (int t = lane; t < nmax; t += 64) c += r[t] >= trial ? 1 : 0;
-      if (wave_sum(c) >= K) res = trial;
+      for (int t = tid; t < nmax; t += 256) c += (staged ? s_v[t] : r[t]) >= trial ? 1 : 0;
+      c = wave_sum(c);
+      if (lane == 0) s_c[b & 1][w] = c;
+      __syncthreads();
+      if (s_c[b & 1][0] + s_c[b & 1][1] + s_c[b & 1][2] + s_c[b & 1][3] >= K) res = trial;
     }
   }
-  if (lane == 0) {
+  if (tid == 0) {
     thr[row] = res;
     cnt[row] = 0;
   }
@@ -926,7 +935,7 @@ void launch_topk_maxima(const ChunkArgs& a, uint32_t* lmax, hipStream_t s) {
 }
 
 void launch_topk_threshold(const ChunkArgs& a, const uint32_t* lmax, uint32_t* thr, int* cnt, hipStream_t s) {
-  k_topk_threshold<<<dim3((a.rows + 3) / 4), dim3(256), 0, s>>>(lmax, a.nvt * kTopkLanes, a.rows, a.k, thr, cnt);
+  k_topk_threshold<<<dim3(a.rows), dim3(256), 0, s>>>(lmax, a.nvt * kTopkLanes, a.k, thr, cnt);
 }
 
 void launch_topk_collect(const ChunkArgs& a, const uint32_t* thr, int* cnt, uint64_t* cand, hipStream_t s) {
