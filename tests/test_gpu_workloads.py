@@ -94,3 +94,26 @@ def test_full_workload_sampled(name):
     e_dw = rel_fro(dW2.cpu().numpy(), ref_b["dW"])
     log(f"case {name}: masked-subset rel_fro dW={e_dw:.3g}")
     assert e_dw <= 1e-2
+
+
+@pytest.mark.timeout(600)
+def test_single_call_full_size_bitwise():
+    """kd_chunked_fwd_bwd at the 32K gpt-oss workload equals kd_chunked_fwd +
+    kd_chunked_bwd bit for bit (same fp32 logits, same dZ formula)."""
+    wl = inputs.workload("gpt-oss-20b-32k")
+    log(f"case single-call {wl.name}: generating")
+    inp = inputs.make_inputs(wl, seed=1)
+    d = upload(inp)
+    log("case single-call: two calls")
+    f = L.forward(d["H"], d["W"], d["t_ids"], d["t_logits"], d["mask"], chunk=wl.chunk)
+    dH, dW = L.backward(d["H"], d["W"], d["t_ids"], d["t_logits"], d["mask"], f["lse"], None, chunk=wl.chunk,
+                        workspace=f["workspace"])
+    torch.cuda.synchronize()
+    del f["workspace"]
+    log("case single-call: one call")
+    g = L.forward_backward(d["H"], d["W"], d["t_ids"], d["t_logits"], d["mask"], None, chunk=wl.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(g["loss"], f["loss"])
+    assert torch.equal(g["lse"], f["lse"])
+    assert torch.equal(g["dH"], dH)
+    assert torch.equal(g["dW"], dW)
