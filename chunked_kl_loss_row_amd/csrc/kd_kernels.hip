@@ -5,6 +5,11 @@
 // "2. Fused Chunked KL Loss"):
 //   forward : k_prep -> k_fwd_proj -> k_merge -> k_loss_fold
 //   backward: k_prep -> k_bwd_dz -> k_bwd_dh (+ k_dh_reduce) -> k_bwd_dw
+//   single call (forward + backward): k_prep -> k_fwd_proj keeping the
+//             chunk's fp32 logits -> k_merge -> k_loss_fold -> k_dz_cached
+//             -> k_bwd_dh (+ k_dh_reduce) -> k_bwd_dw
+//   teacher top-K producer: k_topk_pass<0> (sampled row maxima) ->
+//             k_topk_threshold -> k_topk_pass<1> (candidates) -> k_topk_select
 // The per-chunk logit tile lives only in registers / LDS in the forward; in
 // the backward the closed-form dZ of one chunk is written to the workspace
 // (bounded by the chunk size) and consumed by the two gradient GEMMs.
