@@ -148,7 +148,6 @@ __global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
 // ---------------------------------------------------------------------------
 // helpers shared by the two projection epilogues
 // ---------------------------------------------------------------------------
-// Write the accumulators of the rows in stage half `h` to the fp32 stage.
 // dZ before the teacher term, (g s) exp(z - lse) with lse2 = lse log2(e), and
 // the teacher term's subtraction.  Contraction is off so that every kernel
 // forming dZ (recomputed or cached logits) rounds it the same way.
@@ -161,8 +160,10 @@ __device__ __forceinline__ float dz_sub(float o, float sub) {
   return o - sub;
 }
 
+// Write the accumulators of the rows in stage slice `h` (kStageRows rows) to
+// the fp32 stage.
 template <typename G>
-__device__ __forceinline__ void stage_half(float* stage, const f32x16 (&acc)[G::FM][G::FN], int h) {
+__device__ __forceinline__ void stage_slice(float* stage, const f32x16 (&acc)[G::FM][G::FN], int h) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / (G::BN / G::WN), wn = wave % (G::BN / G::WN);
 #pragma unroll
@@ -183,8 +184,9 @@ __device__ __forceinline__ void stage_half(float* stage, const f32x16 (&acc)[G::
 // Tile (rt, vt): z = H[rt rows] W[vt vocab]^T on matrix cores.  The epilogue
 // stages z (fp32) in LDS, reduces each row to the tile's max and sum of
 // exp(z - max) and copies z at the row's teacher ids that fall in the tile
-// (the gather is a copy of the accumulator, bit for bit).  Logits never reach
-// HBM.
+// (the gather is a copy of the accumulator, bit for bit).  Logits reach HBM
+// only in the single-call path (zc != null), which keeps the chunk's fp32
+// logits in the workspace for the dZ pass.
 template <typename T>
 __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, const T* __restrict__ W,
                                                      int rows, int d, int v, int nvt, int K,
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
   const int g16 = tid >> 4, l16 = tid & 15;
 #pragma unroll
   for (int h = 0; h < G::BM / kStageRows; ++h) {
-    stage_half<G>(stage, acc, h);
+    stage_slice<G>(stage, acc, h);
     lds_barrier();
     for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
       const int row = h * kStageRows + rr, grow = rt * G::BM + row;
@@ -419,7 +421,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
   const bool full_tile = (vt + 1) * G::BN <= v;
 #pragma unroll
   for (int h = 0; h < G::BM / kStageRows; ++h) {
-    stage_half<G>(stage, acc, h);
+    stage_slice<G>(stage, acc, h);
     lds_barrier();
     for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
       const int row = h * kStageRows + rr, grow = rt * G::BM + row;
@@ -731,7 +733,7 @@ __global__ __launch_bounds__(512, 1) void k_topk_pass(const T* __restrict__ H, c
   const int g16 = tid >> 4, l16 = tid & 15;
 #pragma unroll
   for (int h = 0; h < G::BM / kStageRows; ++h) {
-    stage_half<G>(stage, acc, h);
+    stage_slice<G>(stage, acc, h);
     lds_barrier();
     for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
       const int row = h * kStageRows + rr, grow = rt * G::BM + row;
