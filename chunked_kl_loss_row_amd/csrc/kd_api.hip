@@ -33,7 +33,8 @@ bool dtype_ok(int t) { return t == KD_F32 || t == KD_BF16; }
 // Workspace regions, as byte offsets from the aligned base.
 struct Layout {
   int nvt, ldz, split, kslice;
-  size_t keys, psort, zgs, negent, ssum, lb, pm, ps, rl, loss_acc, dz, dhp, zc;
+  size_t keys, psort, zgs, negent, ssum, lb, pm, ps, rl, loss_acc, dz, dhp, zc, ht;
+  int ldt;
   size_t lmax, thr, cnt, cand;  // teacher top-K producer
   size_t total;  // bytes from the aligned base
 };
@@ -70,6 +71,8 @@ Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   L.dz = take(loss ? C * static_cast<size_t>(L.ldz) * xs : 0);
   L.dhp = take(loss && L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
   L.zc = take(mode == Mode::kLossCached ? C * static_cast<size_t>(L.ldz) * 4 : 0);
+  L.ldt = (p.chunk + 7) / 8 * 8;
+  L.ht = take(loss ? static_cast<size_t>(L.ldt) * static_cast<size_t>(p.d) * xs : 0);
   L.lmax = take(loss ? 0 : C * static_cast<size_t>(L.nvt) * kd::kTopkLanes * 4);
   L.thr = take(loss ? 0 : C * 4);
   L.cnt = take(loss ? 0 : C * 4);
@@ -124,7 +127,7 @@ int64_t g_prof_n[KD_K_COUNT];
 const char* const g_prof_names[KD_K_COUNT] = {"prep",      "fwd_proj",       "merge",         "loss_fold",
                                               "bwd_dz",    "bwd_dh",         "dh_reduce",     "bwd_dw",
                                               "dz_cached", "topk_maxima",    "topk_threshold", "topk_collect",
-                                              "topk_select"};
+                                              "topk_select", "h_transpose"};
 
 hipEvent_t prof_event() {
   if (!g_prof_pool.empty()) {
@@ -198,6 +201,8 @@ ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const voi
   a.dh_split = L.split;
   a.dh_kslice = L.kslice;
   a.zc = cached ? reinterpret_cast<float*>(base + L.zc) : nullptr;
+  a.ht = base + L.ht;
+  a.ldt = L.ldt;
   return a;
 }
 
@@ -284,6 +289,7 @@ int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W, const i
     timed(KD_K_BWD_DZ, s, [&] { kd::launch_bwd_dz(a, lse + row0, grad_loss, s); });
     timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
     if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
+    timed(KD_K_H_TRANSPOSE, s, [&] { kd::launch_transpose_h(a, s); });
     timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
   }
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
@@ -327,6 +333,7 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, con
     timed(KD_K_DZ_CACHED, s, [&] { kd::launch_dz_cached(a, lse + row0, grad_loss, s); });
     timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
     if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
+    timed(KD_K_H_TRANSPOSE, s, [&] { kd::launch_transpose_h(a, s); });
     timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
   }
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;

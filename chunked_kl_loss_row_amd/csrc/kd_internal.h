@@ -47,6 +47,8 @@ struct ChunkArgs {
   void* dz;         // [chunk][ldz] dZ in x dtype
   float* dhp;       // [split][chunk][d] split partials of dH
   float* zc;        // [chunk][ldz] fp32 logits kept by the forward (single-call path), else null
+  void* ht;         // [d][ldt] H_c transposed (x dtype), columns [rows, ldt) zero
+  int ldt;          // row stride of ht in elements (chunk rounded up to 8)
   int dh_split;     // number of V slices of the dH reduction
   int dh_kslice;    // V entries per slice (multiple of the k tile)
 };
@@ -61,6 +63,7 @@ void launch_zero_loss(float* loss, hipStream_t s);
 void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);
 void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);
 void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s);
+void launch_transpose_h(const ChunkArgs& a, hipStream_t s);
 void launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s);
 void launch_topk_maxima(const ChunkArgs& a, uint32_t* lmax, hipStream_t s);
 void launch_topk_threshold(const ChunkArgs& a, const uint32_t* lmax, uint32_t* thr, int* cnt, hipStream_t s);

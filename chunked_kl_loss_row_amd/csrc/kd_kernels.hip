@@ -28,7 +28,7 @@ using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3>;
 template <typename T>
 using DhGemm = Gemm<T, kDhBM, kDhBN, true, false>;
 template <typename T>
-using DwGemm = Gemm<T, kDwBM, kDwBN, false, false>;
+using DwGemm = Gemm<T, kDwBM, kDwBN, false, true>;
 static_assert(ProjGemm<uint16_t>::NT == ProjGemm<float>::NT && DhGemm<uint16_t>::NT == DhGemm<float>::NT &&
                   DwGemm<uint16_t>::NT == DwGemm<float>::NT,
               "one block size per kernel for both dtypes");
@@ -594,9 +594,30 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
   *reinterpret_cast<f32x4*>(dH + i4) = s;
 }
 
+// H_c^T for the dW GEMM (its k = chunk row then runs contiguous in memory,
+// so both of its operands need no transposing LDS read for B).  64 x 64
+// tiles through LDS; columns [rows, ldt) are written as zeros, so a 16-byte
+// load that straddles the last row reads zeros.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose_h(const T* __restrict__ Hc, int rows, int d, T* __restrict__ ht,
+                                                     int ldt) {
+  __shared__ T tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;  // c: hidden column, r: chunk row
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < rows && c < d) ? Hc[static_cast<long>(r) * d + c] : T(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < d && r < ldt) ht[static_cast<long>(c) * ldt + r] = tile[tx][i];
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int ldz,
-                                                   const T* __restrict__ Hc, int rows, int d, int v,
+                                                   const T* __restrict__ ht, int ldt, int rows, int d, int v,
                                                    float* __restrict__ dW) {
   using G = DwGemm<T>;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
@@ -605,9 +626,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
   if (t < 0) return;
   const int mt = t / ntn, nt = t % ntn;
   f32x16 acc[G::FM][G::FN];
-  // A(m = vocab, k = chunk row) = dZ[k][m];  B(n = hidden, k = chunk row) = H[k][n]
+  // A(m = vocab, k = chunk row) = dZ[k][m];  B(n = hidden, k = chunk row) = H_c^T[n][k]
   const Operand<T> A{dz, ldz, static_cast<long>(rows) * ldz, mt * G::BM, ldz, rows};
-  const Operand<T> B{Hc, d, static_cast<long>(rows) * d, nt * G::BN, d, rows};
+  const Operand<T> B{ht, ldt, static_cast<long>(d) * ldt, nt * G::BN, d, rows};
   G::run(A, B, 0, rows, smem, acc);
   // dW += acc through LDS, one 64-row slice at a time (atom row s of both
   // wave rows): the slice's accumulators go to LDS, then each wave adds whole
@@ -986,15 +1007,25 @@ void launch_dh_reduce(const ChunkArgs& a, float* dH, hipStream_t s) {
                                                                                        count, dH);
 }
 
+void launch_transpose_h(const ChunkArgs& a, hipStream_t s) {
+  const dim3 grid((a.d + 63) / 64, (a.ldt + 63) / 64), block(256);
+  if (a.x_bf16)
+    k_transpose_h<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H), a.rows, a.d,
+                                                   static_cast<uint16_t*>(a.ht), a.ldt);
+  else
+    k_transpose_h<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), a.rows, a.d,
+                                                static_cast<float*>(a.ht), a.ldt);
+}
+
 void launch_bwd_dw(const ChunkArgs& a, float* dW, hipStream_t s) {
   const int mtn = (a.v + kDwBM - 1) / kDwBM, ntn = (a.d + kDwBN - 1) / kDwBN;
   const dim3 grid(xcd_grid(mtn * ntn)), block(DwGemm<uint16_t>::NT);
   if (a.x_bf16)
     k_bwd_dw<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.dz), a.ldz,
-                                              static_cast<const uint16_t*>(a.H), a.rows, a.d, a.v, dW);
+                                              static_cast<const uint16_t*>(a.ht), a.ldt, a.rows, a.d, a.v, dW);
   else
     k_bwd_dw<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.dz), a.ldz,
-                                           static_cast<const float*>(a.H), a.rows, a.d, a.v, dW);
+                                           static_cast<const float*>(a.ht), a.ldt, a.rows, a.d, a.v, dW);
 }
 
 }  // namespace kd

@@ -31,7 +31,8 @@ typedef enum kd_kernel_kind {
   KD_K_TOPK_THRESHOLD = 10, /* top-K producer: per-row threshold                 */
   KD_K_TOPK_COLLECT = 11,   /* top-K producer: projection + candidate collection */
   KD_K_TOPK_SELECT = 12,    /* top-K producer: per-row sort of the candidates     */
-  KD_K_COUNT = 13
+  KD_K_H_TRANSPOSE = 13,    /* backward: H_c transposed for the dW GEMM          */
+  KD_K_COUNT = 14
 } kd_kernel_kind;
 
 /* Turn event recording on (1) or off (0).  Either way the accumulated
