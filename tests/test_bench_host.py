@@ -1,0 +1,45 @@
+"""Host-side logic of bench.py (CPU only, no GPU call).
+
+* more than one GPU is refused with a message and exit status 2;
+* a committed memory-counter summary is used for roofline.traffic only when it
+  names the dominant kernel and was taken on the current kernel sources;
+* the source digest covers every kernel source file.
+"""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def _summary(tmp_path, kernel, digest, nbytes=123456789):
+    p = tmp_path / "traffic.txt"
+    p.write_text("# comment: ignored\n"
+                 f"kernel: {kernel}\nsource_digest: {digest}\nscaled_bytes_per_launch: {nbytes}\n")
+    return str(p)
+
+
+def test_traffic_read_only_for_matching_kernel_and_sources(tmp_path):
+    dig = bench.source_digest()
+    assert bench.read_traffic(_summary(tmp_path, "bwd_dw", dig), "bwd_dw") == 123456789
+    assert bench.read_traffic(_summary(tmp_path, "bwd_dw", dig), "fwd_proj") is None
+    assert bench.read_traffic(_summary(tmp_path, "bwd_dw", "0" * 16), "bwd_dw") is None
+    assert bench.read_traffic(str(tmp_path / "missing.txt"), "bwd_dw") is None
+
+
+def test_digest_covers_kernel_sources():
+    src = os.path.join(ROOT, "chunked_kl_loss_row_amd", "csrc")
+    names = [n for n in os.listdir(src) if n.endswith((".hip", ".h"))]
+    assert len(names) >= 5
+    assert len(bench.source_digest()) == 16
+    assert bench.source_digest() == bench.source_digest()
