@@ -43,6 +43,11 @@ def make_problem(hidden, weight, t_ids, t_logits, chunk: int) -> B.KDProblem:
     return B.problem(n, d, v, t_ids.shape[1], chunk, _xdtype(hidden), _xdtype(t_logits))
 
 
+def _check_mask(mask, n):
+    if mask is not None and (mask.dtype not in (torch.uint8, torch.bool) or mask.shape != (n,)):
+        raise TypeError("mask must be a uint8 (or bool) tensor of shape [n]")
+
+
 def _check(*ts):
     for t in ts:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
@@ -58,6 +63,7 @@ def forward(hidden, weight, t_ids, t_logits, mask=None, chunk: int = 2048, works
     """Run kd_chunked_fwd; returns {"loss", "lse", "row_loss"?, "zg"?, "workspace"}."""
     _check(hidden, weight, t_ids, t_logits, mask)
     prob = make_problem(hidden, weight, t_ids, t_logits, chunk)
+    _check_mask(mask, prob.n)
     dev = hidden.device
     ws = workspace if workspace is not None else workspace_for(prob, dev)
     out = {"loss": torch.empty(1, dtype=torch.float32, device=dev),
@@ -76,6 +82,7 @@ def backward(hidden, weight, t_ids, t_logits, mask, lse, grad_loss=None, dW=None
     into when given, else a zero buffer is made."""
     _check(hidden, weight, t_ids, t_logits, mask, lse, grad_loss)
     prob = make_problem(hidden, weight, t_ids, t_logits, chunk)
+    _check_mask(mask, prob.n)
     dev = hidden.device
     ws = workspace if workspace is not None else workspace_for(prob, dev)
     if dH is None:
@@ -95,6 +102,7 @@ def forward_backward(hidden, weight, t_ids, t_logits, mask=None, grad_loss=None,
     Returns {"loss", "lse", "dH", "dW", "workspace"}."""
     _check(hidden, weight, t_ids, t_logits, mask, grad_loss)
     prob = make_problem(hidden, weight, t_ids, t_logits, chunk)
+    _check_mask(mask, prob.n)
     dev = hidden.device
     ws = workspace if workspace is not None else torch.empty(B.kd_chunked_fwd_bwd_workspace_size(prob),
                                                              dtype=torch.uint8, device=dev)
