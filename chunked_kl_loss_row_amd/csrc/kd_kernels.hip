@@ -426,11 +426,21 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
     for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
       const int row = h * kStageRows + rr, grow = rt * G::BM + row;
       if (grow >= rows) break;
+      T* out = dz + static_cast<long>(grow) * ldz + vt * G::BN;
+      if (s_live[row] == 0) {  // masked row: exact zeros, whatever its inputs hold
+#pragma unroll
+        for (int jj = 0; jj < G::BN / 64; ++jj) {
+          if constexpr (sizeof(T) == 2)
+            *reinterpret_cast<uint2*>(out + jj * 64 + l16 * 4) = make_uint2(0u, 0u);
+          else
+            *reinterpret_cast<f32x4*>(out + jj * 64 + l16 * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        continue;
+      }
       const float lse2 = s_lse2[row], coef = s_coef[row], gm = s_gm[row];
       const int lo = s_lo[row], n = s_hi[row] - lo;
-      T* out = dz + static_cast<long>(grow) * ldz + vt * G::BN;
       float o[G::BN / 64][4];
-      if (s_live[row] != 0) {
+      {
 #pragma unroll
         for (int jj = 0; jj < G::BN / 64; ++jj) {
           const f32x4 x = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + jj * 64 + l16 * 4);
@@ -464,11 +474,6 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
             for (int e = 0; e < 4; ++e)
               if (vt * G::BN + jj * 64 + l16 * 4 + e >= v) o[jj][e] = 0.f;
         }
-      } else {  // masked row: exact zeros, whatever its inputs hold
-#pragma unroll
-        for (int jj = 0; jj < G::BN / 64; ++jj)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[jj][e] = 0.f;
       }
 #pragma unroll
       for (int jj = 0; jj < G::BN / 64; ++jj) {
