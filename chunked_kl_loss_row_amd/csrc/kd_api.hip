@@ -83,7 +83,7 @@ Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
 
 int check_problem(const kd_problem* p) {
   if (!p) return KD_ERR_NULL;
-  if (p->n < 0 || p->d < 1 || p->v < 1 || p->v > 16777215 || p->k < 1 || p->k > 256 || p->k > p->v ||
+  if (p->n < 0 || p->d < 1 || p->d > 65536 || p->v < 1 || p->v > 16777215 || p->k < 1 || p->k > 256 || p->k > p->v ||
       p->chunk < 1)
     return KD_ERR_SHAPE;
   if (!dtype_ok(p->x_dtype) || !dtype_ok(p->t_dtype)) return KD_ERR_DTYPE;

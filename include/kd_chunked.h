@@ -53,8 +53,8 @@ extern "C" {
 typedef enum kd_status {
   KD_OK = 0,
   KD_ERR_NULL = 1,      /* a required pointer is NULL                          */
-  KD_ERR_SHAPE = 2,     /* n < 0, d < 1, v < 1, k not in [1, min(v,256)],
-                           chunk < 1, v > 16777215                              */
+  KD_ERR_SHAPE = 2,     /* n < 0, d not in [1, 65536], v < 1,
+                           k not in [1, min(v,256)], chunk < 1, v > 16777215     */
   KD_ERR_DTYPE = 3,     /* x_dtype / t_dtype not a kd_dtype                     */
   KD_ERR_ALIGN = 4,     /* d % 8 != 0, or a pointer not 16-byte aligned         */
   KD_ERR_WORKSPACE = 5, /* workspace_bytes < kd_chunked_workspace_size(prob)    */
@@ -66,7 +66,7 @@ typedef enum kd_dtype { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
 
 typedef struct kd_problem {
   int64_t n;       /* positions (batch*seq flattened), >= 0                     */
-  int32_t d;       /* hidden size, multiple of 8                                 */
+  int32_t d;       /* hidden size, multiple of 8, at most 65536                  */
   int32_t v;       /* vocabulary size                                            */
   int32_t k;       /* teacher top-K, 1 <= k <= min(v, 256)                       */
   int32_t chunk;   /* rows per chunk (the only tuning knob), >= 1               */

@@ -68,7 +68,8 @@ def test_workspace_grows_with_chunk_and_dtype():
 
 
 @pytest.mark.parametrize("kw", [dict(n=-1), dict(d=0), dict(v=0), dict(k=0), dict(k=257, v=1000),
-                                dict(k=20, v=10), dict(chunk=0), dict(v=16777216)])
+                                dict(k=20, v=10), dict(chunk=0), dict(v=16777216),
+                                dict(d=65544)])
 def test_bad_shapes(kw):
     prob = P(**kw)
     assert B.kd_chunked_workspace_size(prob) == 0
