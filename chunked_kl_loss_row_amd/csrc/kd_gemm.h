@@ -294,16 +294,33 @@ struct Gemm {
   //             read A[i] for step 0 of tile kt+1.
   __device__ __forceinline__ static void run(const Operand<T>& A, const Operand<T>& B, int k_begin, int k_end,
                                              char* lds, f32x16 (&acc)[FM][FN]) {
+    run(A, B, k_begin, k_end, lds, acc, ZeroAcc{});
+  }
+  struct ZeroAcc {
+    static constexpr bool kLoads = false;
+    __device__ __forceinline__ void operator()(f32x16 (&acc)[FM][FN]) const {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    }
+  };
+  // Same, with acc starting from what `init(acc)` puts there.  An init with
+  // kLoads fills acc with vector memory loads: they are issued after the
+  // prologue's tile loads (so both are in flight together) and the prologue
+  // then waits for every load of the wave, so no wait for them is left for
+  // the compiler to place inside the k loop.
+  template <class Init>
+  __device__ __forceinline__ static void run(const Operand<T>& A, const Operand<T>& B, int k_begin, int k_end,
+                                             char* lds, f32x16 (&acc)[FM][FN], const Init& init) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     const int nk = (k_end - k_begin + BK - 1) / BK;
     if (nk <= 0) {
+      init(acc);
+      if constexpr (Init::kLoads) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
       return;
     }
@@ -321,7 +338,11 @@ struct Gemm {
         lb.issue_all(b, k_begin + t * BK, lds + t * STAGE + A_BYTES, wave);
       }
     }
-    wait_tiles(min(NS - 2, nk - 1));
+    init(acc);
+    if constexpr (Init::kLoads)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    else
+      wait_tiles(min(NS - 2, nk - 1));
     lds_barrier();
     u32x4 af[FM], b0[FN], b1[FN];
 #pragma unroll

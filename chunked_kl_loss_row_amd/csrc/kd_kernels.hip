@@ -620,6 +620,65 @@ __global__ __launch_bounds__(256) void k_transpose_h(const T* __restrict__ Hc, i
   }
 }
 
+// dW tile access in the accumulator layout of one wave.  Used as the
+// engine's accumulator initialiser (loads) and for the write-back.  The
+// fields are wave-uniform; each phase derives its per-lane part afresh from
+// an opaque lane id, so no per-lane value has to stay live across the k loop
+// (all registers are taken there).
+//   row of element (i, e) = rbase + 32 i + 8 (e / 4) + (e % 4) + 4 (lane / 32)
+//   column of atom j      = cbase + 32 j + lane % 32
+// Byte offsets stay below 384 d 4 < 2^31 (d <= 65536); a column past d gets
+// the top bit set, which puts it past any region (read as 0, not written).
+template <class G>
+struct DwTile {
+  static constexpr bool kLoads = true;
+  const F32Region& o;
+  int d, rbase, cbase;
+  struct Lane {
+    int d, rbase, cbase;  // opaque copies of the fields
+    uint32_t base;        // byte offset of the lane's (row, column) in the atom
+    uint32_t oob[G::FN];  // 0, or the top bit for columns past d
+  };
+  // Every input passes through an empty volatile asm, so the values of one
+  // call are not merged with those of another across the k loop.
+  __device__ __forceinline__ Lane lane_part() const {
+    Lane l;
+    uint32_t all = ~0u;
+    l.d = d;
+    l.rbase = rbase;
+    l.cbase = cbase;
+    asm volatile("" : "+s"(all), "+s"(l.d), "+s"(l.rbase), "+s"(l.cbase));
+    const int lane = static_cast<int>(__builtin_amdgcn_mbcnt_hi(all, __builtin_amdgcn_mbcnt_lo(all, 0u)));
+    const int lc = lane & 31;
+    l.base = static_cast<uint32_t>((4 * (lane >> 5) * l.d + lc) * 4);
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) l.oob[j] = lc < l.d - l.cbase - 32 * j ? 0u : kOOB;
+    return l;
+  }
+  __device__ __forceinline__ static uint32_t offset(const Lane& l, int i, int j, int e) {
+    const int urow = l.rbase + 32 * i + 8 * (e >> 2) + (e & 3);
+    return (l.base + static_cast<uint32_t>((urow * l.d + l.cbase + 32 * j) * 4)) | l.oob[j];
+  }
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[G::FM][G::FN]) const {
+    const Lane l = lane_part();
+#pragma unroll
+    for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = o.load(offset(l, i, j, e));
+  }
+  __device__ __forceinline__ void store(const f32x16 (&acc)[G::FM][G::FN]) const {
+    const Lane l = lane_part();
+#pragma unroll
+    for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o.store(acc[i][j][e], offset(l, i, j, e));
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int ldz,
                                                    const T* __restrict__ ht, int ldt, int rows, int d, int v,
@@ -630,55 +689,21 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
   const int t = xcd_tile(blockIdx.x, mtn * ntn);
   if (t < 0) return;
   const int mt = t / ntn, nt = t % ntn;
-  f32x16 acc[G::FM][G::FN];
   // A(m = vocab, k = chunk row) = dZ[k][m];  B(n = hidden, k = chunk row) = H_c^T[n][k]
   const Operand<T> A{dz, ldz, static_cast<long>(rows) * ldz, mt * G::BM, ldz, rows};
   const Operand<T> B{ht, ldt, static_cast<long>(d) * ldt, nt * G::BN, d, rows};
-  G::run(A, B, 0, rows, smem, acc);
-  // dW += acc through LDS, one 64-row slice at a time (atom row s of both
-  // wave rows): the slice's accumulators go to LDS, then each wave adds whole
-  // rows to dW with coalesced 16-byte reads and writes (a lane per 16 bytes,
-  // a wave per 256-column row).  The reads of slice s+1 are issued before
-  // slice s is added; two LDS slice buffers alternate.  Rows past v fall
-  // outside the region; columns past d (a multiple of 4) get kOOB.
-  static_assert(G::BM / G::WM == 2 && G::BN == 256 && G::NT == 512, "slice layout: 2 wave rows, 64 lanes x 16 B");
-  constexpr int PITCH = G::BN + 8;                 // floats per LDS row (rows 4 apart on other banks)
-  constexpr int SLICE = 64 * PITCH;                // floats per slice buffer
-  constexpr int CH = 64 / (G::NT / 64);            // rows (16-byte chunks) per thread per slice
-  static_assert(2 * SLICE * 4 <= G::LDS_BYTES, "two slice buffers must fit in LDS");
+  // dW += dZ^T H_c with the accumulators starting from the tile's current dW
+  // values: they are loaded while the first operand tiles are in flight and
+  // stored back after the last tile, so no read of dW waits after the
+  // products are done.  Rows past v fall outside the region.
   const int row0 = mt * G::BM, col0 = nt * G::BN;
   const F32Region o(dW + static_cast<long>(row0) * d, static_cast<long>(v - row0) * d);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / (G::BN / G::WN), wn = wave % (G::BN / G::WN);
-  float* stage = reinterpret_cast<float*>(smem);
-  const bool col_ok = col0 + 4 * lane < d;
-  auto offset = [&](int s, int u) -> uint32_t {
-    const int lr = wave + (G::NT / 64) * u;  // slice row of this wave's u-th chunk
-    const int row = (lr >> 5) * G::WM + 32 * s + (lr & 31);
-    return col_ok ? static_cast<uint32_t>((row * d + col0 + 4 * lane) * 4) : kOOB;
-  };
-  f32x4 old[2][CH];
-#pragma unroll
-  for (int u = 0; u < CH; ++u) old[0][u] = o.load4(offset(0, u));
-#pragma unroll
-  for (int s = 0; s < G::FM; ++s) {
-    float* buf = stage + (s & 1) * SLICE;
-#pragma unroll
-    for (int j = 0; j < G::FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        buf[(wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * PITCH + acc_col<G>(wn, j, lane)] = acc[s][j][e];
-    lds_barrier();
-    if (s + 1 < G::FM) {
-#pragma unroll
-      for (int u = 0; u < CH; ++u) old[(s + 1) & 1][u] = o.load4(offset(s + 1, u));
-    }
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(buf + (wave + (G::NT / 64) * u) * PITCH + 4 * lane);
-      o.store4(x + old[s & 1][u], offset(s, u));
-    }
-  }
+  const DwTile<G> tile{o, d, wm * G::WM, col0 + wn * G::WN};
+  f32x16 acc[G::FM][G::FN];
+  G::run(A, B, 0, rows, smem, acc, tile);
+  tile.store(acc);
 }
 
 // ---------------------------------------------------------------------------

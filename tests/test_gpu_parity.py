@@ -155,9 +155,13 @@ def test_dw_accumulates_and_keeps_prior_contents():
     base = run_hip(d, 200)["dW"]
     prior = torch.randn(wl.v, wl.d, device="cuda", dtype=torch.float32)
     once = run_hip(d, 200, dW_init=prior)["dW"]
-    torch.testing.assert_close(once, prior + base, rtol=1e-6, atol=1e-6)
+    # The prior contents enter the fp32 accumulators before a chunk's
+    # products, so `once` and `prior + base` round differently: per element
+    # about 35 accumulator updates (3 chunks of at most 200 rows, 16 rows per
+    # update), each off by at most 2^-24 of a magnitude of a few units.
+    torch.testing.assert_close(once, prior + base, rtol=1e-5, atol=1e-5)
     twice = run_hip(d, 200, dW_init=once)["dW"]
-    torch.testing.assert_close(twice, prior + 2 * base, rtol=1e-5, atol=1e-5)
+    torch.testing.assert_close(twice, prior + 2 * base, rtol=2e-5, atol=2e-5)
 
 
 def test_g_scales_gradients():
