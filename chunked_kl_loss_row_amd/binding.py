@@ -21,7 +21,7 @@ KD_F32, KD_BF16 = 0, 1
 # names declared by include/kd_chunked.h and include/kd_profile.h
 EXPORTS = ("kd_chunked_workspace_size", "kd_status_string", "kd_chunked_fwd", "kd_chunked_bwd",
            "kd_chunked_fwd_bwd_workspace_size", "kd_chunked_fwd_bwd", "kd_teacher_topk_workspace_size",
-           "kd_teacher_topk", "kd_profile_enable", "kd_profile_read")
+           "kd_teacher_topk", "kd_chunked_validate", "kd_profile_enable", "kd_profile_read")
 KD_K_COUNT = 14
 
 
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.kd_teacher_topk_workspace_size.restype = ctypes.c_size_t
         L.kd_teacher_topk.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.kd_teacher_topk.restype = ctypes.c_int
+        L.kd_chunked_validate.argtypes = [P, vp, vp, vp, vp]
+        L.kd_chunked_validate.restype = ctypes.c_int
         L.kd_profile_enable.argtypes = [ctypes.c_int]
         L.kd_profile_enable.restype = ctypes.c_int
         L.kd_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -137,6 +139,15 @@ def kd_chunked_bwd(prob: KDProblem, H, W, t_ids, t_logits, mask, lse, grad_loss,
                               _ptr(workspace), wsb, _stream(stream))
     if check and st != KD_OK:
         raise KDError(st, "kd_chunked_bwd")
+    return st
+
+
+def kd_chunked_validate(prob: KDProblem, t_ids, mask, out, stream=None, check: bool = True) -> int:
+    """Enqueue the teacher-record check (see include/kd_chunked.h); ``out``
+    is an int64 [4] device buffer."""
+    st = lib().kd_chunked_validate(ctypes.byref(prob), _ptr(t_ids), _ptr(mask), _ptr(out), _stream(stream))
+    if check and st != KD_OK:
+        raise KDError(st, "kd_chunked_validate")
     return st
 
 

@@ -229,6 +229,22 @@ const char* kd_status_string(int status) {
   }
 }
 
+int kd_chunked_validate(const kd_problem* prob, const int32_t* t_ids, const uint8_t* mask, int64_t* out,
+                        void* stream) {
+  int st = check_problem(prob);
+  if (st != KD_OK) return st;
+  const kd_problem& p = *prob;
+  if (!out || (p.n > 0 && !t_ids)) return KD_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(out) & 7u) != 0) return KD_ERR_ALIGN;
+  if ((p.n + 3) / 4 > 0x7FFFFFFF) return KD_ERR_SHAPE;  // one wave per row, four per workgroup
+  st = check_device();
+  if (st != KD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  kd::launch_validate(t_ids, mask, static_cast<long>(p.n), p.k, p.v, out, s);
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
 int kd_chunked_fwd(const kd_problem* prob, const void* H, const void* W, const int32_t* t_ids,
                    const void* t_logits, const uint8_t* mask, float* loss, float* lse, float* row_loss,
                    float* zg, void* workspace, size_t workspace_bytes, void* stream) {

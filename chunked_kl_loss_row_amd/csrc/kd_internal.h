@@ -64,6 +64,7 @@ void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStre
 void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);
 void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s);
 void launch_transpose_h(const ChunkArgs& a, hipStream_t s);
+void launch_validate(const int32_t* ids, const uint8_t* mask, long n, int K, int v, int64_t* out, hipStream_t s);
 void launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s);
 void launch_topk_maxima(const ChunkArgs& a, uint32_t* lmax, hipStream_t s);
 void launch_topk_threshold(const ChunkArgs& a, const uint32_t* lmax, uint32_t* thr, int* cnt, hipStream_t s);

@@ -136,6 +136,23 @@ def teacher_topk(hidden, weight, k: int = 100, chunk: int = 2048, workspace=None
     return out
 
 
+def validate_teacher(t_ids, v: int, mask=None) -> torch.Tensor:
+    """kd_chunked_validate: checks the teacher record's ids (int32 [n, k])
+    against the vocabulary size ``v`` on unmasked rows.  Returns an int64 [4]
+    device tensor (no synchronisation): rows with an id outside [0, v), rows
+    with a repeated id, and the first row of each kind (-1 if none)."""
+    _check(t_ids, mask)
+    if t_ids.dtype != torch.int32 or t_ids.dim() != 2:
+        raise TypeError("teacher ids must be an int32 tensor [n, k]")
+    n, k = t_ids.shape
+    _check_mask(mask, n)
+    out = torch.empty(4, dtype=torch.int64, device=t_ids.device)
+    # d, chunk and the dtypes play no part in the check; any valid values do
+    prob = B.problem(n, 8, v, k, 1, B.KD_F32)
+    B.kd_chunked_validate(prob, t_ids, mask.view(torch.uint8) if mask is not None else None, out)
+    return out
+
+
 class KDChunkedKL(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, t_ids, t_logits, mask, chunk):

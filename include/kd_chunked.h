@@ -148,6 +148,26 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W,
                        const float* grad_loss, float* loss, float* lse, float* dH, float* dW,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Debug check of the teacher record against what the loss assumes of it.
+ * The cache holds, per position, the K most probable teacher tokens
+ * (agentlenshq.com page, section "1. Top-K Logit Cachingによるオフライン
+ * 蒸留"): K distinct ids of the vocabulary.  The loss calls do not check
+ * this; an id outside [0,v) is never matched, so the result is meaningless.
+ * This call counts, over unmasked rows only (mask NULL = every row):
+ *   out[0]  rows with an id outside [0, prob->v)
+ *   out[1]  rows with an id that occurs more than once in the row
+ *   out[2]  the smallest row counted in out[0], or -1
+ *   out[3]  the smallest row counted in out[1], or -1
+ *   t_ids   [n, k] int32     mask  [n] uint8 or NULL (rows with 0 skipped)
+ *   out     int64 [4], 8-byte aligned, written (prior contents ignored)
+ * Only prob->n, v and k are used (d, chunk and the dtypes are still
+ * checked).  The ids of masked rows are never read.  No workspace.
+ * Returns KD_OK, KD_ERR_NULL (out NULL, or t_ids NULL with n > 0),
+ * KD_ERR_SHAPE, KD_ERR_ALIGN (out), KD_ERR_DEVICE or KD_ERR_LAUNCH; nothing
+ * is enqueued on error. */
+int kd_chunked_validate(const kd_problem* prob, const int32_t* t_ids, const uint8_t* mask,
+                        int64_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

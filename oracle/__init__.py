@@ -8,3 +8,4 @@ from .kd_oracle import (  # noqa: F401
     kd_forward, kd_backward, widen_inputs, run,
 )
 from .topk import teacher_topk  # noqa: F401
+from .validate import validate_teacher  # noqa: F401

@@ -134,6 +134,22 @@ def test_valid_arguments_without_gpu_report_device():
                          workspace_bytes=need, stream=0)
 
 
+def test_validate_argument_errors():
+    fake = 1 << 20
+    st = B.kd_chunked_validate(P(), fake, None, None, stream=0, check=False)
+    assert st == B.KD_ERR_NULL
+    st = B.kd_chunked_validate(P(), None, None, fake, stream=0, check=False)
+    assert st == B.KD_ERR_NULL
+    st = B.kd_chunked_validate(P(), fake, None, fake + 4, stream=0, check=False)
+    assert st == B.KD_ERR_ALIGN
+    st = B.kd_chunked_validate(P(k=0), fake, None, fake, stream=0, check=False)
+    assert st == B.KD_ERR_SHAPE
+    st = B.kd_chunked_validate(P(n=4 * 2 ** 31), fake, None, fake, stream=0, check=False)
+    assert st == B.KD_ERR_SHAPE
+    if not _has_gpu():
+        assert B.kd_chunked_validate(P(), fake, None, fake, stream=0, check=False) == B.KD_ERR_DEVICE
+
+
 def test_profile_hook_without_launches():
     assert B.kd_profile_enable(True) == 0
     allk = B.kd_profile_all()
