@@ -403,13 +403,6 @@ struct F32Region {
   __device__ __forceinline__ void store(float x, uint32_t off) const {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, off, 0, 0);
   }
-  // 16 bytes at a 16-byte aligned offset
-  __device__ __forceinline__ f32x4 load4(uint32_t off) const {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-  }
-  __device__ __forceinline__ void store4(const f32x4& x, uint32_t off) const {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, off, 0, 0);
-  }
 };
 
 // Workgroup -> tile mapping that keeps neighbouring tiles on one XCD.
