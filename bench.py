@@ -183,13 +183,22 @@ def main():
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     B.kd_profile_enable(True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event after each step as well (recording an event does not synchronise):
+    # per-step times for the median / min next to the mean over the timed region
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         step()
+        marks[i].record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    per_step = sorted([e0.elapsed_time(marks[0])] +
+                      [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)])
+    step_stats = {"median": round(per_step[len(per_step) // 2] if len(per_step) % 2 else
+                                  0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2]), 4),
+                  "min": round(per_step[0], 4), "max": round(per_step[-1], 4)}
     kern = B.kd_profile_all()
     B.kd_profile_enable(False)
     peak_gib = torch.cuda.max_memory_allocated() / 2 ** 30
@@ -305,6 +314,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
