@@ -114,7 +114,9 @@ def cpu_baseline(inp, rows_n):
     del np
     return {"value": rows.size / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{rows.size} seeded positions of {wl.name} (fp64 numpy dense forward + backward "
-                      f"incl. their dW contribution), {dt:.1f} s"}
+                      f"incl. their dW contribution), {dt:.1f} s",
+            # linear extrapolation (the oracle's cost is per position): not measured
+            "extrapolated_full_n_s": round(wl.n * dt / rows.size, 1)}
 
 
 def main():
