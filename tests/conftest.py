@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests cannot run without a device: skip them cleanly when collected
-    # on a host without one (they are selected with -m gpu on the GPU machine).
+    # on a host without one (they are selected with -m gpu on an MI355X host).
     try:
         import torch
         has_gpu = torch.cuda.is_available()
