@@ -28,6 +28,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # MI355X published peaks
+# vocabulary entries per projection tile of the library (its per-tile partials
+# and tile bounds scale with ceil(V / this)); a CPU test checks it against the
+# kernel sources
+PROJ_TILE_V = 384
 PEAK_BF16_TFLOPS = 2516.6   # dense bf16 matrix cores: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_F32_TFLOPS = 157.3     # dense fp32 matrix cores
 PEAK_HBM_GBS = 8000.0
@@ -214,7 +218,7 @@ def main():
                    "ms_per_step": t / args.steps} for k, (t, n) in kern.items()}
     # the two stand-alone (memory-bound) passes: algorithmic bytes per step and GB/s
     ts = 2 if wl.t_dtype == "bf16" else 4
-    nvt = -(-V // 256)
+    nvt = -(-V // PROJ_TILE_V)
     alg_bytes = {
         # ids + logits + mask read; sorted (key, p), zeroed gather slots, negent, s, tile bounds written
         "prep": 2 * (N * wl.k * (4 + ts) + N + N * wl.k * 12 + N * 8 + N * (nvt + 1) * 2),

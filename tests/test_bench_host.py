@@ -3,7 +3,9 @@
 * more than one GPU is refused with a message and exit status 2;
 * a committed memory-counter summary is used for roofline.traffic only when it
   names the dominant kernel and was taken on the current kernel sources;
-* the source digest covers every kernel source file.
+* the source digest covers every kernel source file;
+* the projection tile width used for the memory-bound passes' byte counts is
+  the kernels' own.
 """
 import os
 import subprocess
@@ -43,3 +45,10 @@ def test_digest_covers_kernel_sources():
     assert len(names) >= 5
     assert len(bench.source_digest()) == 16
     assert bench.source_digest() == bench.source_digest()
+
+
+def test_projection_tile_width_matches_the_kernels():
+    import re
+    src = open(os.path.join(ROOT, "chunked_kl_loss_row_amd", "csrc", "kd_internal.h")).read()
+    m = re.search(r"constexpr int kProjBN = (\d+);", src)
+    assert m and int(m.group(1)) == bench.PROJ_TILE_V
