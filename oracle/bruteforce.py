@@ -8,6 +8,11 @@ the KL divergence of the renormalised top-K teacher distribution from the
 student distribution at the same K token ids, summed over positions -- not the
 rearranged ``negent - sum p z + s lse`` form the oracle uses.
 
+With a temperature ``tau`` the teacher and student distributions are
+softmaxes of ``a / tau`` and ``z / tau`` and the sum is multiplied by
+``tau^2`` (the usual temperature-scaled distillation loss; the pages name
+loss-choice ablations without defining any); ``tau = 1`` is the plain loss.
+
 Gradients come from central differences of that loss at 50 digits, so they pin
 the closed-form gradient without using it (the pages only say a closed form
 exists: aihot.vn page "Tối ưu hóa chi phí chưng cất tri thức…", section
@@ -24,12 +29,14 @@ def _mp(x):
     return mpmath.mpf(float(x))
 
 
-def loss(H, W, ids, logits, mask=None):
-    """Return ``(L, lse_list, row_loss_list)`` as mpmath numbers.
+def loss(H, W, ids, logits, mask=None, tau=1):
+    """Return ``(L, lse_list, row_loss_list)`` as mpmath numbers (``lse`` of
+    ``z / tau``).
 
     ``H [n][d]``, ``W [v][d]``, ``ids [n][K]``, ``logits [n][K]`` are nested
     sequences of floats/ints (exact values), ``mask`` a sequence of 0/1 or None."""
     with mpmath.workdps(DPS):
+        t = _mp(tau)
         n, d, v = len(H), len(H[0]), len(W)
         Hm = [[_mp(x) for x in row] for row in H]
         Wm = [[_mp(x) for x in row] for row in W]
@@ -41,13 +48,13 @@ def loss(H, W, ids, logits, mask=None):
                 acc = mpmath.mpf(0)
                 for c in range(d):
                     acc += Hm[i][c] * Wm[j][c]
-                z.append(acc)
+                z.append(acc / t)
             partition = mpmath.fsum(mpmath.exp(zj) for zj in z)
             lses.append(mpmath.log(partition))
             if mask is not None and not mask[i]:
                 rls.append(mpmath.mpf(0))
                 continue
-            a = [_mp(x) for x in logits[i]]
+            a = [_mp(x) / t for x in logits[i]]
             za = mpmath.fsum(mpmath.exp(x) for x in a)
             row = mpmath.mpf(0)
             for kk in range(len(a)):
@@ -55,12 +62,13 @@ def loss(H, W, ids, logits, mask=None):
                 q = mpmath.exp(z[int(ids[i][kk])]) / partition
                 if p != 0:
                     row += p * mpmath.log(p / q)
+            row *= t * t
             rls.append(row)
             total += row
         return total, lses, rls
 
 
-def grad_fd(H, W, ids, logits, mask=None, g=1.0, step="1e-20"):
+def grad_fd(H, W, ids, logits, mask=None, g=1.0, step="1e-20", tau=1):
     """Central-difference gradient of ``g * L`` w.r.t. every entry of H and W.
 
     Returns ``(dH, dW)`` as nested lists of mpmath numbers."""
@@ -72,7 +80,7 @@ def grad_fd(H, W, ids, logits, mask=None, g=1.0, step="1e-20"):
 
         def L(Hx, Wx):
             with mpmath.workdps(DPS):
-                return _loss_mp(Hx, Wx, ids, logits, mask)
+                return _loss_mp(Hx, Wx, ids, logits, mask, _mp(tau))
 
         dH = [[None] * len(Hm[0]) for _ in Hm]
         for i in range(len(Hm)):
@@ -97,19 +105,19 @@ def grad_fd(H, W, ids, logits, mask=None, g=1.0, step="1e-20"):
         return dH, dW
 
 
-def _loss_mp(Hm, Wm, ids, logits, mask):
+def _loss_mp(Hm, Wm, ids, logits, mask, t):
     """Same sum as ``loss`` on mpmath matrices (no widening)."""
     total = mpmath.mpf(0)
     for i in range(len(Hm)):
         if mask is not None and not mask[i]:
             continue
-        z = [mpmath.fsum(Hm[i][c] * Wm[j][c] for c in range(len(Hm[i]))) for j in range(len(Wm))]
+        z = [mpmath.fsum(Hm[i][c] * Wm[j][c] for c in range(len(Hm[i]))) / t for j in range(len(Wm))]
         partition = mpmath.fsum(mpmath.exp(zj) for zj in z)
-        a = [_mp(x) for x in logits[i]]
+        a = [_mp(x) / t for x in logits[i]]
         za = mpmath.fsum(mpmath.exp(x) for x in a)
         for kk in range(len(a)):
             p = mpmath.exp(a[kk]) / za
             q = mpmath.exp(z[int(ids[i][kk])]) / partition
             if p != 0:
                 total += p * mpmath.log(p / q)
-    return total
+    return total * t * t

@@ -20,7 +20,7 @@ vocabulary-by-position grid -- written out in fp64 with numpy:
   "LLMのための効率的な知識蒸留…", section
   "1. Top-K Logit Cachingによるオフライン蒸留").  Reading: the teacher
   distribution is the softmax of those K logits, renormalised over the K
-  entries, temperature 1, no bucket for the remaining mass.
+  entries, no bucket for the remaining mass.
 * student: logits ``z_i = W h_i`` over the full vocabulary (the loss owns the
   output projection: agentlenshq.com page, section "2. Fused Chunked KL Loss"),
   log-probabilities ``log q_iv = z_iv - lse_i`` normalised over all V.
@@ -32,6 +32,13 @@ vocabulary-by-position grid -- written out in fp64 with numpy:
   được").  From the definition above,
   ``dL/dz_iv = g m_i (s_i q_iv - sum_k p_ik [t_ik = v])`` with
   ``s_i = sum_k p_ik``; then ``dH = dZ W`` and ``dW = dZ^T H``.
+* temperature (a loss variant; the pages name loss-choice ablations without
+  defining any): reading: the usual temperature-scaled distillation loss.
+  Teacher ``p = softmax(a / tau)`` over the K entries, student
+  ``q = softmax(z / tau)`` over V, ``L = tau^2 sum_i m_i KL(p_i || q_i)`` at
+  the K ids; ``lse_i = log sum_v exp(z_iv / tau)``; the gathered logits stay
+  ``z``; ``dL/dz_iv = g tau m_i (s_i q_iv - sum_k p_ik [t_ik = v])``.
+  ``tau = 1`` is the loss above.
 
 Rows are processed in blocks only to bound host memory; rows are independent,
 so the blocking does not change any value beyond fp64 rounding order of the
@@ -68,14 +75,15 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # teacher side
 # ----------------------------------------------------------------------------
-def teacher_distribution(t_logits: np.ndarray):
+def teacher_distribution(t_logits: np.ndarray, tau: float = 1.0):
     """Renormalised top-K teacher distribution of each row.
 
-    ``p_ik = exp(a_ik - max_j a_ij) / sum_j exp(a_ij - max_j a_ij)``;
-    returns ``p [n,K]``, ``negent [n] = sum_k p_ik log p_ik`` (``0 log 0 = 0``)
-    and ``s [n] = sum_k p_ik``.  Cached top-K record: agentlenshq.com page,
+    ``p_ik = exp(a_ik - max_j a_ij) / sum_j exp(a_ij - max_j a_ij)`` with the
+    logits divided by ``tau`` first; returns ``p [n,K]``,
+    ``negent [n] = sum_k p_ik log p_ik`` (``0 log 0 = 0``) and
+    ``s [n] = sum_k p_ik``.  Cached top-K record: agentlenshq.com page,
     section "1. Top-K Logit Cachingによるオフライン蒸留"."""
-    a = np.asarray(t_logits, dtype=np.float64)
+    a = np.asarray(t_logits, dtype=np.float64) / tau
     amax = a.max(axis=1, keepdims=True)
     e = np.exp(a - amax)
     p = e / e.sum(axis=1, keepdims=True)
@@ -109,14 +117,14 @@ def _mask_rows(mask: Optional[np.ndarray], rows: np.ndarray) -> np.ndarray:
 
 def kd_forward(H: np.ndarray, W: np.ndarray, t_ids: np.ndarray, t_logits: np.ndarray,
                mask: Optional[np.ndarray] = None, rows: Optional[Sequence[int]] = None,
-               block: int = 256) -> dict:
+               block: int = 256, tau: float = 1.0) -> dict:
     """Dense forward on fp64 inputs (already widened).
 
     ``rows`` restricts the evaluation to a subset of positions (rows are
     independent); ``loss`` is then the sum over that subset.  Masked rows
     contribute 0 and their teacher record is not read.
-    Returns ``loss`` (python float, summed with ``math.fsum``), ``lse``,
-    ``zg [r,K]``, ``row_loss``."""
+    Returns ``loss`` (python float, summed with ``math.fsum``), ``lse`` (of
+    ``z / tau``), ``zg [r,K]`` (the logits ``z`` at the ids), ``row_loss``."""
     n = H.shape[0]
     rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
     K = t_ids.shape[1]
@@ -127,7 +135,7 @@ def kd_forward(H: np.ndarray, W: np.ndarray, t_ids: np.ndarray, t_logits: np.nda
     for b0 in range(0, rows.size, block):
         sel = rows[b0:b0 + block]
         z = student_logits(H[sel], W)
-        lse_b = row_logsumexp(z)
+        lse_b = row_logsumexp(z / tau)
         lse[b0:b0 + sel.size] = lse_b
         live = m[b0:b0 + sel.size] != 0
         if not live.any():
@@ -135,10 +143,10 @@ def kd_forward(H: np.ndarray, W: np.ndarray, t_ids: np.ndarray, t_logits: np.nda
         li = np.nonzero(live)[0]
         ids = np.asarray(t_ids[sel[li]], dtype=np.int64)
         zg_b = np.take_along_axis(z[li], ids, axis=1)
-        p, negent, s = teacher_distribution(t_logits[sel[li]])
+        p, negent, s = teacher_distribution(t_logits[sel[li]], tau)
         zg[b0 + li] = zg_b
-        # sum_k p (log p - (z_t - lse)) = negent - sum_k p z_t + s * lse
-        row_loss[b0 + li] = negent - (p * zg_b).sum(axis=1) + s * lse_b[li]
+        # tau^2 sum_k p (log p - (z_t / tau - lse)) = tau^2 (negent - sum_k p z_t / tau + s * lse)
+        row_loss[b0 + li] = tau * tau * (negent - (p * zg_b).sum(axis=1) / tau + s * lse_b[li])
     return {"loss": math.fsum(row_loss.tolist()), "lse": lse, "zg": zg,
             "row_loss": row_loss, "rows": rows}
 
@@ -149,10 +157,10 @@ def kd_forward(H: np.ndarray, W: np.ndarray, t_ids: np.ndarray, t_logits: np.nda
 def kd_backward(H: np.ndarray, W: np.ndarray, t_ids: np.ndarray, t_logits: np.ndarray,
                 mask: Optional[np.ndarray] = None, g: float = 1.0,
                 rows: Optional[Sequence[int]] = None, want_dw: bool = True,
-                want_dz: bool = False, block: int = 256) -> dict:
+                want_dz: bool = False, block: int = 256, tau: float = 1.0) -> dict:
     """Gradient of ``g * L`` for the positions in ``rows`` (default: all).
 
-    ``dZ_iv = g m_i (s_i exp(z_iv - lse_i) - sum_k p_ik [t_ik = v])``;
+    ``dZ_iv = g tau m_i (s_i exp(z_iv / tau - lse_i) - sum_k p_ik [t_ik = v])``;
     ``dH_i = dZ_i W`` (one row per requested position) and
     ``dW = sum_{i in rows} dZ_i^T h_i`` (the contribution of those rows; equal
     to the full dW when the mask is zero outside them).  The p-scatter uses
@@ -171,14 +179,14 @@ def kd_backward(H: np.ndarray, W: np.ndarray, t_ids: np.ndarray, t_logits: np.nd
         if live.size == 0:
             continue
         hs = H[sel[live]]
-        z = student_logits(hs, W)
+        z = student_logits(hs, W) / tau
         lse_b = row_logsumexp(z)
-        p, _, s = teacher_distribution(t_logits[sel[live]])
+        p, _, s = teacher_distribution(t_logits[sel[live]], tau)
         dz = s[:, None] * np.exp(z - lse_b[:, None])
         r_idx = np.repeat(np.arange(live.size), p.shape[1])
         np.add.at(dz, (r_idx, np.asarray(t_ids[sel[live]], dtype=np.int64).ravel()),
                   -p.ravel())
-        dz *= g
+        dz *= g * tau
         dH[b0 + live] = dz @ W
         if want_dw:
             dW += dz.T @ hs
@@ -207,11 +215,12 @@ def widen_inputs(inp: dict) -> dict:
     }
 
 
-def run(inp: dict, g: float = 1.0, rows=None, want_dw: bool = True, block: int = 256) -> dict:
+def run(inp: dict, g: float = 1.0, rows=None, want_dw: bool = True, block: int = 256,
+        tau: float = 1.0) -> dict:
     """Forward and backward of one stored input dict, all in fp64."""
     x = widen_inputs(inp)
-    f = kd_forward(x["H"], x["W"], x["t_ids"], x["t_logits"], x["mask"], rows=rows, block=block)
+    f = kd_forward(x["H"], x["W"], x["t_ids"], x["t_logits"], x["mask"], rows=rows, block=block, tau=tau)
     b = kd_backward(x["H"], x["W"], x["t_ids"], x["t_logits"], x["mask"], g=g, rows=rows,
-                    want_dw=want_dw, block=block)
+                    want_dw=want_dw, block=block, tau=tau)
     f.update(b)
     return f

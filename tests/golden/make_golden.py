@@ -1,4 +1,5 @@
-"""Write tests/golden/tiny_bruteforce.json (run from the repository root).
+"""Write tests/golden/tiny_bruteforce.json and tiny_bruteforce_tau.json (run
+from the repository root).
 
 The pages print no worked example, so the stored values are computed here by
 the 50-digit brute-force implementation in ``oracle/bruteforce.py`` (plain
@@ -45,6 +46,30 @@ def main():
             "dH": [[s(x) for x in r] for r in dH], "dW": [[s(x) for x in r] for r in dW],
         })
     path = os.path.join(ROOT, "tests", "golden", "tiny_bruteforce.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print("wrote", path)
+
+    # temperature: the same brute force with the teacher and student logits
+    # divided by tau and the sum multiplied by tau^2 (the usual
+    # temperature-scaled distillation loss; the pages name loss-choice
+    # ablations without defining them)
+    out = {"source": "oracle/bruteforce.py at 50 digits with a temperature tau: teacher softmax(a / tau), "
+                     "student softmax(z / tau), tau^2 times the KL at the K ids",
+           "cases": []}
+    for (name, n, d, v, k, seed, masked), tau in [(TINY[0], 2.5), (TINY[2], 0.6), (TINY[3], 1.7)]:
+        H, W, ids, a, mask = tiny_problem(n, d, v, k, seed, masked)
+        mk = None if mask is None else mask.tolist()
+        L, lses, rls = bruteforce.loss(H.tolist(), W.tolist(), ids.tolist(), a.tolist(), mk, tau=tau)
+        dH, dW = bruteforce.grad_fd(H.tolist(), W.tolist(), ids.tolist(), a.tolist(), mk, g=0.37, tau=tau)
+        out["cases"].append({
+            "name": f"{name}-tau{tau}", "n": n, "d": d, "v": v, "k": k, "seed": seed, "masked": list(masked),
+            "H": H.tolist(), "W": W.tolist(), "t_ids": ids.tolist(), "t_logits": a.tolist(),
+            "g": 0.37, "tau": tau,
+            "loss": s(L), "lse": [s(x) for x in lses], "row_loss": [s(x) for x in rls],
+            "dH": [[s(x) for x in r] for r in dH], "dW": [[s(x) for x in r] for r in dW],
+        })
+    path = os.path.join(ROOT, "tests", "golden", "tiny_bruteforce_tau.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print("wrote", path)

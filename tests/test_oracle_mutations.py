@@ -4,8 +4,9 @@ Each mutation edits one line of ``oracle/kd_oracle.py``'s source text (a
 dropped term, a wrong sign, a wrong index, a transposed operand, an inverted
 mask), loads the edited copy as a separate module, and runs the pins that do
 not depend on the oracle itself: the 50-digit brute-force fixture (values and
-central-difference gradients), the zero-loss construction and the dZ / dW
-sum-to-zero invariants.  Every mutation must fail at least one of them.
+central-difference gradients, at temperature 1 and at three other
+temperatures), the zero-loss construction and the dZ / dW sum-to-zero
+invariants.  Every mutation must fail at least one of them.
 """
 import json
 import os
@@ -27,12 +28,12 @@ MUTATIONS = [
      "return np.log(np.exp(z - m[:, None]).sum(axis=1))"),
     ("lse is the max", "return m + np.log(np.exp(z - m[:, None]).sum(axis=1))", "return m"),
     ("wrong vocab row", "return h_rows @ w.T", "return h_rows @ np.roll(w, 1, axis=0).T"),
-    ("gather sign", "row_loss[b0 + li] = negent - (p * zg_b).sum(axis=1) + s * lse_b[li]",
-     "row_loss[b0 + li] = negent + (p * zg_b).sum(axis=1) + s * lse_b[li]"),
-    ("dropped entropy term", "row_loss[b0 + li] = negent - (p * zg_b).sum(axis=1) + s * lse_b[li]",
-     "row_loss[b0 + li] = - (p * zg_b).sum(axis=1) + s * lse_b[li]"),
-    ("dropped lse term", "row_loss[b0 + li] = negent - (p * zg_b).sum(axis=1) + s * lse_b[li]",
-     "row_loss[b0 + li] = negent - (p * zg_b).sum(axis=1)"),
+    ("gather sign", "(negent - (p * zg_b).sum(axis=1) / tau + s * lse_b[li])",
+     "(negent + (p * zg_b).sum(axis=1) / tau + s * lse_b[li])"),
+    ("dropped entropy term", "(negent - (p * zg_b).sum(axis=1) / tau + s * lse_b[li])",
+     "(- (p * zg_b).sum(axis=1) / tau + s * lse_b[li])"),
+    ("dropped lse term", "(negent - (p * zg_b).sum(axis=1) / tau + s * lse_b[li])",
+     "(negent - (p * zg_b).sum(axis=1) / tau)"),
     ("gather off by one", "zg_b = np.take_along_axis(z[li], ids, axis=1)",
      "zg_b = np.take_along_axis(z[li], (ids + 1) % z.shape[1], axis=1)"),
     ("mask inverted", "return (np.asarray(mask)[rows] != 0).astype(np.float64)",
@@ -44,6 +45,14 @@ MUTATIONS = [
     ("g ignored", "dz *= g", "dz *= 1.0"),
     ("dH transposed operand", "dH[b0 + live] = dz @ W", "dH[b0 + live] = dz @ W[::-1]"),
     ("dW wrong rows", "dW += dz.T @ hs", "dW += dz.T @ hs[::-1]"),
+    # temperature handling (caught by the tau != 1 brute-force cases)
+    ("tau^2 dropped", "row_loss[b0 + li] = tau * tau * (", "row_loss[b0 + li] = ("),
+    ("teacher not tempered", "a = np.asarray(t_logits, dtype=np.float64) / tau",
+     "a = np.asarray(t_logits, dtype=np.float64)"),
+    ("student lse not tempered", "lse_b = row_logsumexp(z / tau)", "lse_b = row_logsumexp(z)"),
+    ("gathered logit not tempered", "(p * zg_b).sum(axis=1) / tau", "(p * zg_b).sum(axis=1)"),
+    ("backward logits not tempered", "z = student_logits(hs, W) / tau", "z = student_logits(hs, W)"),
+    ("gradient tau factor dropped", "dz *= g * tau", "dz *= g"),
 ]
 
 
@@ -56,8 +65,11 @@ def _load_mutant(old, new):
 
 
 def _golden():
-    with open(os.path.join(HERE, "golden", "tiny_bruteforce.json")) as f:
-        return json.load(f)["cases"]
+    cases = []
+    for name in ("tiny_bruteforce.json", "tiny_bruteforce_tau.json"):
+        with open(os.path.join(HERE, "golden", name)) as f:
+            cases += json.load(f)["cases"]
+    return cases
 
 
 def _f(x):
@@ -74,11 +86,12 @@ def pins(mod):
         if c["masked"]:
             mask = np.ones(c["n"], np.uint8)
             mask[c["masked"]] = 0
-        f = mod.kd_forward(H, W, ids, a, mask)
+        tau = c.get("tau", 1.0)
+        f = mod.kd_forward(H, W, ids, a, mask, tau=tau)
         L = _f(c["loss"])
         assert abs(f["loss"] - L) <= 1e-12 * abs(L)
         np.testing.assert_allclose(f["lse"], [_f(x) for x in c["lse"]], rtol=1e-13)
-        b = mod.kd_backward(H, W, ids, a, mask, g=c["g"], want_dz=True)
+        b = mod.kd_backward(H, W, ids, a, mask, g=c["g"], want_dz=True, tau=tau)
         dH = np.array([[_f(x) for x in r] for r in c["dH"]])
         dW = np.array([[_f(x) for x in r] for r in c["dW"]])
         assert np.linalg.norm(b["dH"] - dH) <= 1e-10 * np.linalg.norm(dH)

@@ -27,8 +27,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def _golden():
-    with open(os.path.join(HERE, "golden", "tiny_bruteforce.json")) as f:
-        return json.load(f)["cases"]
+    cases = []
+    for name in ("tiny_bruteforce.json", "tiny_bruteforce_tau.json"):
+        with open(os.path.join(HERE, "golden", name)) as f:
+            cases += json.load(f)["cases"]
+    return cases
 
 
 def _arr(x):
@@ -51,7 +54,7 @@ def test_golden_bruteforce_forward(case):
     if case["masked"]:
         mask = np.ones(case["n"], np.uint8)
         mask[case["masked"]] = 0
-    f = oracle.kd_forward(H, W, ids, a, mask)
+    f = oracle.kd_forward(H, W, ids, a, mask, tau=case.get("tau", 1.0))
     assert abs(f["loss"] - float(mpmath.mpf(case["loss"]))) <= 1e-13 * abs(float(mpmath.mpf(case["loss"])))
     np.testing.assert_allclose(f["lse"], [float(mpmath.mpf(x)) for x in case["lse"]], rtol=1e-14)
     np.testing.assert_allclose(f["row_loss"], [float(mpmath.mpf(x)) for x in case["row_loss"]],
@@ -66,7 +69,7 @@ def test_golden_bruteforce_gradient(case):
     if case["masked"]:
         mask = np.ones(case["n"], np.uint8)
         mask[case["masked"]] = 0
-    b = oracle.kd_backward(H, W, ids, a, mask, g=case["g"])
+    b = oracle.kd_backward(H, W, ids, a, mask, g=case["g"], tau=case.get("tau", 1.0))
     assert rel(b["dH"], _arr(case["dH"])) <= 1e-12
     assert rel(b["dW"], _arr(case["dW"])) <= 1e-12
 
@@ -295,3 +298,49 @@ def test_torch_fp64_autograd():
     assert abs(f["loss"] - L.item()) <= 1e-12 * L.item()
     assert rel(b["dH"], Ht.grad.numpy()) <= 1e-12
     assert rel(b["dW"], Wt.grad.numpy()) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# temperature
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("tau", [0.5, 1.7, 4.0])
+def test_temperature_is_a_rescaling(tau):
+    """L_tau(H, a) = tau^2 L_1(H / tau, a / tau), dH_tau = tau dH_1(H / tau),
+    dW_tau = tau^2 dW_1(H / tau): the tempered loss against the plain one."""
+    H, W, ids, a, mask = _rand_problem()
+    g = 0.37
+    f = oracle.kd_forward(H, W, ids, a, mask, tau=tau)
+    b = oracle.kd_backward(H, W, ids, a, mask, g=g, tau=tau)
+    f1 = oracle.kd_forward(H / tau, W, ids, a / tau, mask)
+    b1 = oracle.kd_backward(H / tau, W, ids, a / tau, mask, g=g)
+    assert abs(f["loss"] - tau * tau * f1["loss"]) <= 1e-12 * abs(f["loss"])
+    np.testing.assert_allclose(f["lse"], f1["lse"], rtol=1e-13)
+    np.testing.assert_allclose(f["zg"], tau * f1["zg"], rtol=1e-13, atol=1e-13)
+    assert rel(b["dH"], tau * b1["dH"]) <= 1e-12
+    assert rel(b["dW"], tau * tau * b1["dW"]) <= 1e-12
+
+
+def test_temperature_torch_fp64_autograd():
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    H, W, ids, a, mask = _rand_problem()
+    g, tau = 0.37, 2.3
+    Ht = torch.tensor(H, dtype=torch.float64, requires_grad=True)
+    Wt = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    live = torch.tensor(np.nonzero(mask)[0])
+    logq = F.log_softmax((Ht @ Wt.T) / tau, dim=1)
+    logq_t = torch.gather(logq[live], 1, torch.tensor(ids)[live])
+    p = torch.softmax(torch.tensor(a, dtype=torch.float64)[live] / tau, dim=1)
+    L = tau * tau * F.kl_div(logq_t, p, reduction="sum")
+    (g * L).backward()
+    f = oracle.kd_forward(H, W, ids, a, mask, tau=tau)
+    b = oracle.kd_backward(H, W, ids, a, mask, g=g, tau=tau)
+    assert abs(f["loss"] - L.item()) <= 1e-12 * L.item()
+    assert rel(b["dH"], Ht.grad.numpy()) <= 1e-12
+    assert rel(b["dW"], Wt.grad.numpy()) <= 1e-12
+
+
+def test_temperature_one_is_the_plain_loss():
+    H, W, ids, a, mask = _rand_problem()
+    f, f1 = oracle.kd_forward(H, W, ids, a, mask, tau=1.0), oracle.kd_forward(H, W, ids, a, mask)
+    assert f["loss"] == f1["loss"] and np.array_equal(f["lse"], f1["lse"])
