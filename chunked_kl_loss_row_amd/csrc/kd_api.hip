@@ -87,6 +87,8 @@ int check_problem(const kd_problem* p) {
       p->chunk < 1)
     return KD_ERR_SHAPE;
   if (!dtype_ok(p->x_dtype) || !dtype_ok(p->t_dtype)) return KD_ERR_DTYPE;
+  // temperature: 0 means 1; otherwise a finite value in [0.01, 100]
+  if (!(p->tau == 0.f || (p->tau >= 0.01f && p->tau <= 100.f))) return KD_ERR_SHAPE;
   if (p->d % 8 != 0) return KD_ERR_ALIGN;
   return KD_OK;
 }
@@ -174,6 +176,7 @@ ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const voi
   ChunkArgs a{};
   const size_t xs = p.x_dtype == KD_BF16 ? 2 : 4, ts = p.t_dtype == KD_BF16 ? 2 : 4;
   a.rows = rows;
+  a.tau = p.tau == 0.f ? 1.f : p.tau;
   a.d = p.d;
   a.v = p.v;
   a.k = p.k;

@@ -27,6 +27,7 @@ struct ChunkArgs {
   int nvt;       // vocabulary tiles of the projection (ceil(v / kProjBN))
   int ldz;       // row stride of dZ in elements (nvt * kProjBN)
   int x_bf16;    // 1: H, W, dZ are bf16; 0: fp32
+  float tau;     // temperature (1: the plain loss)
   int t_bf16;    // 1: teacher logits are bf16; 0: fp32
   const void* H;
   const void* W;

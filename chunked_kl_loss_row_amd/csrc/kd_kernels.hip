@@ -43,8 +43,9 @@ constexpr int proj_smem_bytes() { return G::LDS_BYTES > kStageBytes ? G::LDS_BYT
 // ---------------------------------------------------------------------------
 // teacher record -> renormalised distribution, id-sorted keys, tile ranges
 // ---------------------------------------------------------------------------
-// One wave per row.  p = softmax of the K cached teacher logits (the top-K
-// record renormalised over its entries); negent = sum p log p; s = sum p.
+// One wave per row.  p = softmax of the K cached teacher logits divided by
+// the temperature (the top-K record renormalised over its entries);
+// negent = sum p log p; s = sum p.
 // keys = (id << 8 | k) sorted ascending with p / zg slots in the same order;
 // lb[t] = index of the first key whose id lies in vocabulary tile >= t, so
 // the keys falling in tile t are [lb[t], lb[t+1]).  Masked rows read
@@ -53,7 +54,7 @@ template <typename TT>
 __global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
                                               const TT* __restrict__ logits,
                                               const uint8_t* __restrict__ mask, int rows, int K,
-                                              int nvt, uint32_t* __restrict__ keys,
+                                              int nvt, float inv_tau, uint32_t* __restrict__ keys,
                                               float* __restrict__ psort, float* __restrict__ zgs,
                                               float* __restrict__ negent, float* __restrict__ ssum,
                                               uint16_t* __restrict__ lb) {
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int k = lane + 64 * q;
-      e[q] = (k < K) ? expf(a[q] - amax) : 0.f;
+      e[q] = (k < K) ? expf((a[q] - amax) * inv_tau) : 0.f;
       z += e[q];
     }
     z = wave_sum(z);
@@ -148,12 +149,13 @@ __global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
 // ---------------------------------------------------------------------------
 // helpers shared by the two projection epilogues
 // ---------------------------------------------------------------------------
-// dZ before the teacher term, (g s) exp(z - lse) with lse2 = lse log2(e), and
-// the teacher term's subtraction.  Contraction is off so that every kernel
-// forming dZ (recomputed or cached logits) rounds it the same way.
-__device__ __forceinline__ float dz_exp(float z, float coef, float lse2) {
+// dZ before the teacher term, coef exp(z / tau - lse) with coef = g s tau,
+// t2 = log2(e) / tau and lse2 = lse log2(e) (lse of z / tau), and the teacher
+// term's subtraction.  Contraction is off so that every kernel forming dZ
+// (recomputed or cached logits) rounds it the same way.
+__device__ __forceinline__ float dz_exp(float z, float coef, float lse2, float t2) {
 #pragma clang fp contract(off)
-  return coef * fast_exp2(fmaf(z, kLog2e, -lse2));
+  return coef * fast_exp2(fmaf(z, t2, -lse2));
 }
 __device__ __forceinline__ float dz_sub(float o, float sub) {
 #pragma clang fp contract(off)
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
                                                      const uint32_t* __restrict__ keys,
                                                      float* __restrict__ zgs, float* __restrict__ pm,
                                                      float* __restrict__ ps, float* __restrict__ zc,
-                                                     int ldz) {
+                                                     int ldz, float t2) {
   using G = ProjGemm<T>;
   __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
 #pragma unroll
       for (int j = 0; j < G::BN / 64; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm += fast_exp2((x[j][e] - mx) * kLog2e);
+        for (int e = 0; e < 4; ++e) sm += fast_exp2((x[j][e] - mx) * t2);  // t2 = log2(e) / tau
       sm = group16_sum(sm);
       if (l16 == 0) {
         pm[static_cast<long>(grow) * nvt + vt] = mx;
@@ -285,8 +287,9 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
 // ---------------------------------------------------------------------------
 // forward: merge tile partials -> lse, row loss, gathered logits
 // ---------------------------------------------------------------------------
-// lse_i = M + log sum_t s_t exp(m_t - M) over the vocabulary tiles (fixed
-// order).  row_loss_i = m_i (negent_i - sum_k p_ik zg_ik + s_i lse_i), the
+// lse_i = M / tau + log sum_t s_t exp((m_t - M) / tau) over the vocabulary
+// tiles (fixed order): the lse of z / tau.  row_loss_i =
+// tau^2 m_i (negent_i - sum_k p_ik zg_ik / tau + s_i lse_i), tau^2 times the
 // KL of the renormalised teacher from the student at the K ids.
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm, const float* __restrict__ ps,
                                                int nvt, const uint32_t* __restrict__ keys,
@@ -296,7 +299,8 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm, con
                                                const float* __restrict__ ssum,
                                                const uint8_t* __restrict__ mask, int rows, int K,
                                                float* __restrict__ lse_out, float* __restrict__ rl_out,
-                                               float* __restrict__ zg_out, double* __restrict__ rl_ws) {
+                                               float* __restrict__ zg_out, double* __restrict__ rl_ws,
+                                               float t2, double inv_tau, double tau2) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + w;
   if (row >= rows) return;
@@ -305,16 +309,17 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm, con
   for (int t = lane; t < nvt; t += 64) M = fmaxf(M, pm[pb + t]);
   M = wave_max(M);
   float S = 0.f;
-  for (int t = lane; t < nvt; t += 64) S += ps[pb + t] * fast_exp2((pm[pb + t] - M) * kLog2e);
+  for (int t = lane; t < nvt; t += 64) S += ps[pb + t] * fast_exp2((pm[pb + t] - M) * t2);
   S = wave_sum(S);
-  const double lse = static_cast<double>(M) + log(static_cast<double>(S));
+  const double lse = static_cast<double>(M) * inv_tau + log(static_cast<double>(S));
   const bool live = (mask == nullptr || mask[row] != 0);
   const long kb = static_cast<long>(row) * K;
   double dot = 0.0;
   if (live)
     for (int j = lane; j < K; j += 64) dot += static_cast<double>(psort[kb + j]) * static_cast<double>(zgs[kb + j]);
   dot = wave_sum(dot);
-  const double rl = live ? static_cast<double>(negent[row]) - dot + static_cast<double>(ssum[row]) * lse : 0.0;
+  const double rl =
+      live ? tau2 * (static_cast<double>(negent[row]) - dot * inv_tau + static_cast<double>(ssum[row]) * lse) : 0.0;
   if (lane == 0) {
     lse_out[row] = static_cast<float>(lse);
     rl_ws[row] = rl;
@@ -356,9 +361,9 @@ __global__ void k_zero_loss(float* loss) { loss[0] = 0.f; }
 // ---------------------------------------------------------------------------
 // backward: recompute the projection and form the closed-form dZ
 // ---------------------------------------------------------------------------
-// dZ_iv = g m_i (s_i exp(z_iv - lse_i) - sum_k p_ik [t_ik = v]), evaluated in
-// fp32 as (g s_i) exp(z_iv - lse_i) - g p_ik, the -g p terms applied before
-// the single rounding to the storage dtype.  Masked rows and columns in
+// dZ_iv = g tau m_i (s_i exp(z_iv / tau - lse_i) - sum_k p_ik [t_ik = v]),
+// evaluated in fp32 as (g s_i tau) exp(z_iv / tau - lse_i) - p_ik (g tau),
+// the teacher terms applied before the single rounding to the storage dtype.  Masked rows and columns in
 // [v, ldz) (padding of the row) are written as exact zeros.
 template <typename T>
 __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, const T* __restrict__ W,
@@ -369,7 +374,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
                                                    const float* __restrict__ ssum,
                                                    const uint8_t* __restrict__ mask,
                                                    const float* __restrict__ lse,
-                                                   const float* __restrict__ gptr, T* __restrict__ dz) {
+                                                   const float* __restrict__ gptr, T* __restrict__ dz,
+                                                   float t2, float tau) {
   using G = ProjGemm<T>;
   __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
@@ -394,8 +400,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
       if (live) {
         lo = lb[static_cast<long>(gr) * (nvt + 1) + vt];
         hi = lb[static_cast<long>(gr) * (nvt + 1) + vt + 1];
-        gm = g;
-        coef = g * ssum[gr];  // g folded into the row coefficient
+        gm = g * tau;
+        coef = g * ssum[gr] * tau;  // g and tau folded into the row coefficient
       }
     }
     s_lo[r] = lo;
@@ -445,7 +451,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
         for (int jj = 0; jj < G::BN / 64; ++jj) {
           const f32x4 x = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + jj * 64 + l16 * 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[jj][e] = dz_exp(x[e], coef, lse2);
+          for (int e = 0; e < 4; ++e) o[jj][e] = dz_exp(x[e], coef, lse2, t2);
         }
         // p of the row's teacher ids in this tile, subtracted before the single
         // rounding (c: column in the tile relative to this lane's first one)
@@ -504,7 +510,8 @@ __global__ __launch_bounds__(256) void k_dz_cached(const float* __restrict__ zc,
                                                    const float* __restrict__ ssum,
                                                    const uint8_t* __restrict__ mask,
                                                    const float* __restrict__ lse,
-                                                   const float* __restrict__ gptr, T* __restrict__ dz) {
+                                                   const float* __restrict__ gptr, T* __restrict__ dz,
+                                                   float t2, float tau) {
   const int per_row = ldz / 8;
   const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= static_cast<long>(rows) * per_row) return;
@@ -512,13 +519,13 @@ __global__ __launch_bounds__(256) void k_dz_cached(const float* __restrict__ zc,
   float o[8];
   if (mask == nullptr || mask[row] != 0) {
     const float g = gptr ? gptr[0] : 1.f;
-    const float lse2 = lse[row] * kLog2e, coef = g * ssum[row];
+    const float lse2 = lse[row] * kLog2e, coef = g * ssum[row] * tau, gt = g * tau;
     const f32x4 z0 = *reinterpret_cast<const f32x4*>(zc + static_cast<long>(row) * ldz + c0);
     const f32x4 z1 = *reinterpret_cast<const f32x4*>(zc + static_cast<long>(row) * ldz + c0 + 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      o[e] = dz_exp(z0[e], coef, lse2);
-      o[e + 4] = dz_exp(z1[e], coef, lse2);
+      o[e] = dz_exp(z0[e], coef, lse2, t2);
+      o[e + 4] = dz_exp(z1[e], coef, lse2, t2);
     }
     const int t = c0 / kProjBN;
     const int lo = lb[static_cast<long>(row) * (nvt + 1) + t], hi = lb[static_cast<long>(row) * (nvt + 1) + t + 1];
@@ -526,7 +533,7 @@ __global__ __launch_bounds__(256) void k_dz_cached(const float* __restrict__ zc,
       const long kq = static_cast<long>(row) * K + q;
       const int c = static_cast<int>(keys[kq] >> 8) - c0;
       if (static_cast<unsigned>(c) < 8u) {
-        const float sub = psort[kq] * g;
+        const float sub = psort[kq] * gt;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = dz_sub(o[e], (c == e) ? sub : 0.f);
       }
@@ -919,10 +926,11 @@ void launch_prep(const ChunkArgs& a, hipStream_t s) {
   const dim3 grid((a.rows + 3) / 4), block(256);
   if (a.t_bf16)
     k_prep<uint16_t><<<grid, block, 0, s>>>(a.ids, static_cast<const uint16_t*>(a.logits), a.mask, a.rows,
-                                            a.k, a.nvt, a.keys, a.psort, a.zgs, a.negent, a.ssum, a.lb);
+                                            a.k, a.nvt, 1.0f / a.tau, a.keys, a.psort, a.zgs, a.negent,
+                                            a.ssum, a.lb);
   else
     k_prep<float><<<grid, block, 0, s>>>(a.ids, static_cast<const float*>(a.logits), a.mask, a.rows, a.k,
-                                         a.nvt, a.keys, a.psort, a.zgs, a.negent, a.ssum, a.lb);
+                                         a.nvt, 1.0f / a.tau, a.keys, a.psort, a.zgs, a.negent, a.ssum, a.lb);
 }
 
 void launch_fwd_proj(const ChunkArgs& a, hipStream_t s) {
@@ -931,17 +939,19 @@ void launch_fwd_proj(const ChunkArgs& a, hipStream_t s) {
   if (a.x_bf16)
     k_fwd_proj<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
                                                 static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v,
-                                                a.nvt, a.k, a.lb, a.keys, a.zgs, a.pm, a.ps, a.zc, a.ldz);
+                                                a.nvt, a.k, a.lb, a.keys, a.zgs, a.pm, a.ps, a.zc, a.ldz,
+                                                kLog2e / a.tau);
   else
     k_fwd_proj<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
                                              a.rows, a.d, a.v, a.nvt, a.k, a.lb, a.keys, a.zgs, a.pm,
-                                             a.ps, a.zc, a.ldz);
+                                             a.ps, a.zc, a.ldz, kLog2e / a.tau);
 }
 
 void launch_merge(const ChunkArgs& a, float* lse, float* row_loss, float* zg, hipStream_t s) {
   k_merge<<<dim3((a.rows + 3) / 4), dim3(256), 0, s>>>(a.pm, a.ps, a.nvt, a.keys, a.psort, a.zgs, a.negent,
                                                       a.ssum, a.mask, a.rows, a.k, lse, row_loss, zg,
-                                                      a.rl);
+                                                      a.rl, kLog2e / a.tau, 1.0 / static_cast<double>(a.tau),
+                                                      static_cast<double>(a.tau) * static_cast<double>(a.tau));
 }
 
 void launch_loss_fold(const ChunkArgs& a, int first, int last, float* loss, hipStream_t s) {
@@ -957,11 +967,12 @@ void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStre
     k_bwd_dz<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
                                               static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
                                               a.k, a.ldz, a.lb, a.keys, a.psort, a.ssum, a.mask, lse, g,
-                                              static_cast<uint16_t*>(a.dz));
+                                              static_cast<uint16_t*>(a.dz), kLog2e / a.tau, a.tau);
   else
     k_bwd_dz<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
                                            a.rows, a.d, a.v, a.nvt, a.k, a.ldz, a.lb, a.keys, a.psort,
-                                           a.ssum, a.mask, lse, g, static_cast<float*>(a.dz));
+                                           a.ssum, a.mask, lse, g, static_cast<float*>(a.dz), kLog2e / a.tau,
+                                           a.tau);
 }
 
 void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s) {
@@ -969,10 +980,12 @@ void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipS
   const dim3 grid(static_cast<unsigned>((threads + 255) / 256)), block(256);
   if (a.x_bf16)
     k_dz_cached<uint16_t><<<grid, block, 0, s>>>(a.zc, a.ldz, a.rows, a.v, a.k, a.nvt, a.lb, a.keys, a.psort,
-                                                 a.ssum, a.mask, lse, g, static_cast<uint16_t*>(a.dz));
+                                                 a.ssum, a.mask, lse, g, static_cast<uint16_t*>(a.dz), kLog2e / a.tau,
+                                                 a.tau);
   else
     k_dz_cached<float><<<grid, block, 0, s>>>(a.zc, a.ldz, a.rows, a.v, a.k, a.nvt, a.lb, a.keys, a.psort,
-                                              a.ssum, a.mask, lse, g, static_cast<float*>(a.dz));
+                                              a.ssum, a.mask, lse, g, static_cast<float*>(a.dz), kLog2e / a.tau,
+                                              a.tau);
 }
 
 void launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s) {

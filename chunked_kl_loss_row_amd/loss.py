@@ -29,7 +29,7 @@ def _xdtype(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
 
 
-def make_problem(hidden, weight, t_ids, t_logits, chunk: int) -> B.KDProblem:
+def make_problem(hidden, weight, t_ids, t_logits, chunk: int, temperature: float = 1.0) -> B.KDProblem:
     n, d = hidden.shape
     v, d2 = weight.shape
     if d2 != d:
@@ -40,7 +40,7 @@ def make_problem(hidden, weight, t_ids, t_logits, chunk: int) -> B.KDProblem:
         raise TypeError("hidden and weight must share a dtype")
     if t_ids.dtype != torch.int32:
         raise TypeError("teacher ids must be int32")
-    return B.problem(n, d, v, t_ids.shape[1], chunk, _xdtype(hidden), _xdtype(t_logits))
+    return B.problem(n, d, v, t_ids.shape[1], chunk, _xdtype(hidden), _xdtype(t_logits), temperature)
 
 
 def _check_mask(mask, n):
@@ -59,10 +59,10 @@ def workspace_for(prob: B.KDProblem, device) -> torch.Tensor:
 
 
 def forward(hidden, weight, t_ids, t_logits, mask=None, chunk: int = 2048, workspace=None,
-            row_loss: bool = False, zg: bool = False) -> dict:
+            row_loss: bool = False, zg: bool = False, temperature: float = 1.0) -> dict:
     """Run kd_chunked_fwd; returns {"loss", "lse", "row_loss"?, "zg"?, "workspace"}."""
     _check(hidden, weight, t_ids, t_logits, mask)
-    prob = make_problem(hidden, weight, t_ids, t_logits, chunk)
+    prob = make_problem(hidden, weight, t_ids, t_logits, chunk, temperature)
     _check_mask(mask, prob.n)
     dev = hidden.device
     ws = workspace if workspace is not None else workspace_for(prob, dev)
@@ -77,11 +77,12 @@ def forward(hidden, weight, t_ids, t_logits, mask=None, chunk: int = 2048, works
 
 
 def backward(hidden, weight, t_ids, t_logits, mask, lse, grad_loss=None, dW=None, chunk: int = 2048,
-             workspace=None, dH=None):
+             workspace=None, dH=None, temperature: float = 1.0):
     """Run kd_chunked_bwd; returns (dH, dW).  ``dW`` (fp32) is accumulated
-    into when given, else a zero buffer is made."""
+    into when given, else a zero buffer is made.  ``temperature`` must be the
+    forward's."""
     _check(hidden, weight, t_ids, t_logits, mask, lse, grad_loss)
-    prob = make_problem(hidden, weight, t_ids, t_logits, chunk)
+    prob = make_problem(hidden, weight, t_ids, t_logits, chunk, temperature)
     _check_mask(mask, prob.n)
     dev = hidden.device
     ws = workspace if workspace is not None else workspace_for(prob, dev)
@@ -96,12 +97,12 @@ def backward(hidden, weight, t_ids, t_logits, mask, lse, grad_loss=None, dW=None
 
 
 def forward_backward(hidden, weight, t_ids, t_logits, mask=None, grad_loss=None, dW=None,
-                     chunk: int = 2048, workspace=None, dH=None) -> dict:
+                     chunk: int = 2048, workspace=None, dH=None, temperature: float = 1.0) -> dict:
     """kd_chunked_fwd_bwd: loss, lse, dH and dW (accumulated into ``dW`` when
     given) in one call, each chunk's logits kept instead of recomputed.
     Returns {"loss", "lse", "dH", "dW", "workspace"}."""
     _check(hidden, weight, t_ids, t_logits, mask, grad_loss)
-    prob = make_problem(hidden, weight, t_ids, t_logits, chunk)
+    prob = make_problem(hidden, weight, t_ids, t_logits, chunk, temperature)
     _check_mask(mask, prob.n)
     dev = hidden.device
     ws = workspace if workspace is not None else torch.empty(B.kd_chunked_fwd_bwd_workspace_size(prob),
@@ -155,10 +156,11 @@ def validate_teacher(t_ids, v: int, mask=None) -> torch.Tensor:
 
 class KDChunkedKL(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, hidden, weight, t_ids, t_logits, mask, chunk):
-        out = forward(hidden, weight, t_ids, t_logits, mask, chunk)
+    def forward(ctx, hidden, weight, t_ids, t_logits, mask, chunk, temperature):
+        out = forward(hidden, weight, t_ids, t_logits, mask, chunk, temperature=temperature)
         ctx.save_for_backward(hidden, weight, t_ids, t_logits, mask, out["lse"])
         ctx.chunk = chunk
+        ctx.temperature = temperature
         ctx.workspace = out["workspace"]
         return out["loss"][0]
 
@@ -167,13 +169,15 @@ class KDChunkedKL(torch.autograd.Function):
         hidden, weight, t_ids, t_logits, mask, lse = ctx.saved_tensors
         gl = g.reshape(1).to(torch.float32).contiguous()
         dH, dW = backward(hidden, weight, t_ids, t_logits, mask, lse, gl, chunk=ctx.chunk,
-                          workspace=ctx.workspace)
+                          workspace=ctx.workspace, temperature=ctx.temperature)
         ctx.workspace = None
         gh = dH if hidden.dtype == torch.float32 else dH.to(hidden.dtype)
         gw = dW if weight.dtype == torch.float32 else dW.to(weight.dtype)
-        return gh, gw, None, None, None, None
+        return gh, gw, None, None, None, None, None
 
 
-def kd_chunked_kl(hidden, weight, t_ids, t_logits, mask=None, chunk: int = 2048):
-    """0-d fp32 loss; differentiable w.r.t. ``hidden`` and ``weight``."""
-    return KDChunkedKL.apply(hidden, weight, t_ids, t_logits, mask, chunk)
+def kd_chunked_kl(hidden, weight, t_ids, t_logits, mask=None, chunk: int = 2048, temperature: float = 1.0):
+    """0-d fp32 loss; differentiable w.r.t. ``hidden`` and ``weight``.
+    ``temperature`` tau: tau^2 KL(softmax(a / tau) || softmax(z / tau)) at the
+    K ids (1: the plain loss)."""
+    return KDChunkedKL.apply(hidden, weight, t_ids, t_logits, mask, chunk, temperature)

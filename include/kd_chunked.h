@@ -23,6 +23,16 @@
  * học sinh thu được":  dL/dz_iv = m_i (s_i q_iv - sum_k p_ik [t_ik = v]),
  * s_i = sum_k p_ik, q_i = softmax(z_i).
  *
+ * Temperature (kd_problem.tau), a loss variant.  The aihot.vn page (section
+ * "Mô hình học sinh thu được") reports ablations over the choice of loss
+ * without defining any; reading: the usual temperature-scaled distillation
+ * loss.  With tau != 1 the teacher and student distributions
+ * are softmaxes of a / tau and z / tau and the loss is multiplied by tau^2:
+ *     L = tau^2 sum_i m_i sum_k p_ik (log p_ik - z_{i,t_ik} / tau + lse_i),
+ *     lse_i = log sum_v e^{z_iv / tau},
+ *     dL/dz_iv = tau m_i (s_i q_iv - sum_k p_ik [t_ik = v]), q_i = softmax(z_i / tau).
+ * tau = 1 (or 0, read as 1) is the loss above, with the same arithmetic.
+ *
  * Conventions for every entry point:
  *  - all tensor pointers are DEVICE pointers on the current HIP device, dense
  *    row-major, and 16-byte aligned;
@@ -54,7 +64,8 @@ typedef enum kd_status {
   KD_OK = 0,
   KD_ERR_NULL = 1,      /* a required pointer is NULL                          */
   KD_ERR_SHAPE = 2,     /* n < 0, d not in [1, 65536], v < 1,
-                           k not in [1, min(v,256)], chunk < 1, v > 16777215     */
+                           k not in [1, min(v,256)], chunk < 1, v > 16777215,
+                           tau neither 0 nor in [0.01, 100]                     */
   KD_ERR_DTYPE = 3,     /* x_dtype / t_dtype not a kd_dtype                     */
   KD_ERR_ALIGN = 4,     /* d % 8 != 0, or a pointer not 16-byte aligned         */
   KD_ERR_WORKSPACE = 5, /* workspace_bytes < kd_chunked_workspace_size(prob)    */
@@ -72,6 +83,7 @@ typedef struct kd_problem {
   int32_t chunk;   /* rows per chunk (the only tuning knob), >= 1               */
   int32_t x_dtype; /* kd_dtype of H and W (the projection's compute dtype)      */
   int32_t t_dtype; /* kd_dtype of the teacher logits                            */
+  float tau;       /* temperature: 0 or 1 = the plain loss, else in [0.01, 100]  */
 } kd_problem;
 
 /* Bytes of workspace the fwd and bwd calls need for `prob`.  Depends on
@@ -94,8 +106,9 @@ const char* kd_status_string(int status);
  *   mask     [n]    uint8     0 = position ignored (its teacher record is not
  *                             read), NULL = every position counts
  *   loss     [1]    float     out: L (fixed-order fp64 reduction, then fp32)
- *   lse      [n]    float     out: lse_i for every row, masked ones included
- *   row_loss [n]    float     out (optional, NULL = skip): m_i * KL_i
+ *   lse      [n]    float     out: lse_i (of z_i / tau) for every row, masked
+ *                             ones included
+ *   row_loss [n]    float     out (optional, NULL = skip): tau^2 m_i KL_i
  *   zg       [n,k]  float     out (optional, NULL = skip): z_{i,t_ik}, the
  *                             projection's own fp32 accumulator value; 0 on
  *                             masked rows
@@ -106,10 +119,10 @@ int kd_chunked_fwd(const kd_problem* prob, const void* H, const void* W,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward.  Recomputes each chunk's logits, forms
- *   dZ_iv = g m_i (s_i exp(z_iv - lse_i) - sum_k p_ik [t_ik = v])
+ *   dZ_iv = g tau m_i (s_i exp(z_iv / tau - lse_i) - sum_k p_ik [t_ik = v])
  * in fp32 and rounds it once to x_dtype (the -p terms are applied before the
  * rounding), then dH_c = dZ_c W and dW += dZ_c^T H_c with fp32 accumulation.
- *   H, W, t_ids, t_logits, mask   as for the forward (same values)
+ *   H, W, t_ids, t_logits, mask   as for the forward (same values, same tau)
  *   lse       [n]   float    the forward's lse output
  *   grad_loss [1]   float    device scalar g (upstream gradient), NULL = 1
  *   dH        [n,d] float    out, overwritten; masked rows are exactly zero

@@ -10,8 +10,9 @@ rearranged ``negent - sum p z + s lse`` form the oracle uses.
 
 With a temperature ``tau`` the teacher and student distributions are
 softmaxes of ``a / tau`` and ``z / tau`` and the sum is multiplied by
-``tau^2`` (the usual temperature-scaled distillation loss; the pages name
-loss-choice ablations without defining any); ``tau = 1`` is the plain loss.
+``tau^2`` (the usual temperature-scaled distillation loss; the aihot.vn page,
+section "Mô hình học sinh thu được", reports loss-choice ablations without
+defining any); ``tau = 1`` is the plain loss.
 
 Gradients come from central differences of that loss at 50 digits, so they pin
 the closed-form gradient without using it (the pages only say a closed form

@@ -32,8 +32,9 @@ vocabulary-by-position grid -- written out in fp64 with numpy:
   được").  From the definition above,
   ``dL/dz_iv = g m_i (s_i q_iv - sum_k p_ik [t_ik = v])`` with
   ``s_i = sum_k p_ik``; then ``dH = dZ W`` and ``dW = dZ^T H``.
-* temperature (a loss variant; the pages name loss-choice ablations without
-  defining any): reading: the usual temperature-scaled distillation loss.
+* temperature, a loss variant: the aihot.vn page (section "Mô hình học sinh
+  thu được") reports ablations over the choice of loss without defining any;
+  reading: the usual temperature-scaled distillation loss.
   Teacher ``p = softmax(a / tau)`` over the K entries, student
   ``q = softmax(z / tau)`` over V, ``L = tau^2 sum_i m_i KL(p_i || q_i)`` at
   the K ids; ``lse_i = log sum_v exp(z_iv / tau)``; the gathered logits stay

@@ -52,8 +52,9 @@ def main():
 
     # temperature: the same brute force with the teacher and student logits
     # divided by tau and the sum multiplied by tau^2 (the usual
-    # temperature-scaled distillation loss; the pages name loss-choice
-    # ablations without defining them)
+    # temperature-scaled distillation loss; the aihot.vn page, section
+    # "Mô hình học sinh thu được", reports loss-choice ablations without
+    # defining any)
     out = {"source": "oracle/bruteforce.py at 50 digits with a temperature tau: teacher softmax(a / tau), "
                      "student softmax(z / tau), tau^2 times the KL at the K ids",
            "cases": []}

@@ -33,15 +33,16 @@ def upload(inp):
     }
 
 
-def run_hip(d, chunk, g=None, mask="default", dW_init=None, zg=True, row_loss=True, workspace=None):
+def run_hip(d, chunk, g=None, mask="default", dW_init=None, zg=True, row_loss=True, workspace=None,
+            temperature=1.0):
     """Forward + backward on the GPU; returns numpy results."""
     m = d["mask"] if isinstance(mask, str) else mask
     f = L.forward(d["H"], d["W"], d["t_ids"], d["t_logits"], m, chunk=chunk, row_loss=row_loss, zg=zg,
-                  workspace=workspace)
+                  workspace=workspace, temperature=temperature)
     gl = None if g is None else torch.tensor([g], dtype=torch.float32, device="cuda")
     dW = None if dW_init is None else dW_init.clone()
     dH, dW = L.backward(d["H"], d["W"], d["t_ids"], d["t_logits"], m, f["lse"], gl, dW=dW, chunk=chunk,
-                        workspace=f["workspace"])
+                        workspace=f["workspace"], temperature=temperature)
     torch.cuda.synchronize()
     out = {"loss": float(f["loss"].item()), "lse": f["lse"].cpu().numpy(), "dH": dH, "dW": dW}
     if row_loss:

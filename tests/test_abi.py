@@ -48,8 +48,8 @@ def test_status_strings():
     assert "unknown" in B.kd_status_string(99)
 
 
-def P(n=1000, d=128, v=4096, k=16, chunk=64, x=B.KD_BF16, t=None):
-    return B.problem(n, d, v, k, chunk, x, t)
+def P(n=1000, d=128, v=4096, k=16, chunk=64, x=B.KD_BF16, t=None, tau=1.0):
+    return B.problem(n, d, v, k, chunk, x, t, tau)
 
 
 def test_workspace_independent_of_n():
@@ -69,7 +69,8 @@ def test_workspace_grows_with_chunk_and_dtype():
 
 @pytest.mark.parametrize("kw", [dict(n=-1), dict(d=0), dict(v=0), dict(k=0), dict(k=257, v=1000),
                                 dict(k=20, v=10), dict(chunk=0), dict(v=16777216),
-                                dict(d=65544)])
+                                dict(d=65544), dict(tau=-1.0), dict(tau=0.005), dict(tau=101.0),
+                                dict(tau=float("nan")), dict(tau=float("inf"))])
 def test_bad_shapes(kw):
     prob = P(**kw)
     assert B.kd_chunked_workspace_size(prob) == 0
@@ -158,3 +159,13 @@ def test_profile_hook_without_launches():
     with pytest.raises(B.KDError):
         B.kd_profile_read(B.KD_K_COUNT)
     assert B.kd_profile_enable(False) == 0
+
+
+def test_temperature_zero_reads_as_one():
+    assert B.kd_chunked_workspace_size(P(tau=0.0)) == B.kd_chunked_workspace_size(P(tau=1.0)) > 0
+    assert B.kd_chunked_workspace_size(P(tau=0.01)) > 0 and B.kd_chunked_workspace_size(P(tau=100.0)) > 0
+
+
+def test_problem_struct_layout():
+    # int64 n, six int32 fields, float tau: 36 bytes padded to the int64 alignment
+    assert ctypes.sizeof(B.KDProblem) == 40 and B.KDProblem.tau.offset == 32
