@@ -103,3 +103,61 @@ def test_gather_bit_exact_tempered():
     torch.cuda.synchronize()
     ref = oracle.kd_forward(H.astype(np.float64), W.astype(np.float64), ids, a.astype(np.float64), tau=1.7)
     np.testing.assert_array_equal(f["zg"].cpu().numpy().astype(np.float64), ref["zg"])
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_gpt_oss_full_size_tempered_sampled():
+    """The 32K gpt-oss workload in full at tau = 2 in the bench's launch
+    configuration, checked on 256 seeded rows (lse, row loss, dH) and, with
+    the mask restricted to those rows, the loss and the whole dW; plus the
+    size-independent properties (L >= 0, loss = sum of row losses, vanishing
+    vocabulary sums of dW)."""
+    import math
+    tau = 2.0
+    wl = inputs.workload("gpt-oss-20b-32k")
+    log(f"case gpt-oss tau={tau}: generating inputs")
+    inp = inputs.make_inputs(wl, seed=0)
+    d = upload(inp)
+    log("case gpt-oss tempered: full forward + backward")
+    f = L.forward(d["H"], d["W"], d["t_ids"], d["t_logits"], d["mask"], chunk=wl.chunk, row_loss=True,
+                  temperature=tau)
+    dH, dW = L.backward(d["H"], d["W"], d["t_ids"], d["t_logits"], d["mask"], f["lse"], None, chunk=wl.chunk,
+                        workspace=f["workspace"], temperature=tau)
+    torch.cuda.synchronize()
+    loss = float(f["loss"].item())
+    rl_all = f["row_loss"].cpu().numpy()
+    assert loss >= 0.0 and rel(loss, math.fsum(rl_all.astype(np.float64).tolist())) <= 1e-5
+    col = dW.double().sum(dim=0).abs().max().item()
+    assert col <= 1e-3 * dW.double().abs().sum(dim=0).max().item()
+    rows = inputs.sample_rows(wl.n, 256, seed=3)
+    rows_t = torch.from_numpy(rows).cuda()
+    lse = f["lse"][rows_t].cpu().numpy()
+    dH_s = dH[rows_t].cpu().numpy()
+    del dH, dW
+    log("case gpt-oss tempered: oracle on 256 rows")
+    Hs = oracle.widen(inp["H"][rows], wl.x_dtype)
+    Wx = oracle.widen(inp["W"], wl.x_dtype)
+    ids_s, lg_s = inp["t_ids"][rows], oracle.widen(inp["t_logits"][rows], wl.t_dtype)
+    m_s = inp["mask"][rows]
+    ref_f = oracle.kd_forward(Hs, Wx, ids_s, lg_s, m_s, tau=tau)
+    np.testing.assert_allclose(lse, ref_f["lse"], rtol=1e-5, atol=0)
+    assert np.all(np.abs(rl_all[rows] - ref_f["row_loss"]) <= 1e-3 * (1.0 + np.abs(ref_f["row_loss"])))
+    ref_b = oracle.kd_backward(Hs, Wx, ids_s, lg_s, m_s, want_dw=True, tau=tau)
+    e_dh = rel_fro(dH_s, ref_b["dH"])
+    log(f"case gpt-oss tempered: sampled rows rel_fro dH={e_dh:.3g}")
+    assert e_dh <= 1e-2
+    sub = np.zeros(wl.n, dtype=np.uint8)
+    sub[rows] = 1
+    sub &= inp["mask"]
+    sub_t = torch.from_numpy(sub).cuda()
+    f2 = L.forward(d["H"], d["W"], d["t_ids"], d["t_logits"], sub_t, chunk=wl.chunk, workspace=f["workspace"],
+                   temperature=tau)
+    _, dW2 = L.backward(d["H"], d["W"], d["t_ids"], d["t_logits"], sub_t, f2["lse"], None, chunk=wl.chunk,
+                        workspace=f["workspace"], temperature=tau)
+    torch.cuda.synchronize()
+    ref_loss2 = math.fsum(ref_f["row_loss"][sub[rows] != 0].tolist())
+    assert rel(float(f2["loss"].item()), ref_loss2) <= 1e-3
+    e_dw = rel_fro(dW2.cpu().numpy(), ref_b["dW"])
+    log(f"case gpt-oss tempered: masked-subset rel_fro dW={e_dw:.3g}")
+    assert e_dw <= 1e-2
