@@ -315,7 +315,7 @@ struct Gemm {
   template <class Init>
   __device__ __forceinline__ static void run(const Operand<T>& A, const Operand<T>& B, int k_begin, int k_end,
                                              char* lds, f32x16 (&acc)[FM][FN], const Init& init) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int nk = (k_end - k_begin + BK - 1) / BK;
     if (nk <= 0) {
