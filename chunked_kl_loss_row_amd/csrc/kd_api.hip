@@ -89,6 +89,16 @@ int check_problem(const kd_problem* p) {
   if (!dtype_ok(p->x_dtype) || !dtype_ok(p->t_dtype)) return KD_ERR_DTYPE;
   // temperature: 0 means 1; otherwise a finite value in [0.01, 100]
   if (!(p->tau == 0.f || (p->tau >= 0.01f && p->tau <= 100.f))) return KD_ERR_SHAPE;
+  // The matrix-core tiles address a k-contiguous operand panel (256 rows of
+  // its leading dimension) with 32-bit byte offsets: dZ (leading dimension
+  // 384 * ceil(v / 384)) in dH and the transposed H_c (the chunk rounded up to
+  // 8) in dW must stay below 2^31 bytes per panel.
+  if (dtype_ok(p->x_dtype)) {
+    const int64_t xs = p->x_dtype == KD_BF16 ? 2 : 4;
+    const int64_t ldz = (static_cast<int64_t>(p->v) + kd::kProjBN - 1) / kd::kProjBN * kd::kProjBN;
+    const int64_t ldt = (static_cast<int64_t>(p->chunk) + 7) / 8 * 8;
+    if (256 * ldz * xs > 0x7FFFFFF0LL || 256 * ldt * xs > 0x7FFFFFF0LL) return KD_ERR_SHAPE;
+  }
   if (p->d % 8 != 0) return KD_ERR_ALIGN;
   return KD_OK;
 }

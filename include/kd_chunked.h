@@ -65,7 +65,9 @@ typedef enum kd_status {
   KD_ERR_NULL = 1,      /* a required pointer is NULL                          */
   KD_ERR_SHAPE = 2,     /* n < 0, d not in [1, 65536], v < 1,
                            k not in [1, min(v,256)], chunk < 1, v > 16777215,
-                           tau neither 0 nor in [0.01, 100]                     */
+                           tau neither 0 nor in [0.01, 100], or a 32-bit tile
+                           offset limit: v > 4194048 or chunk > 4194296 for
+                           bf16, v > 2097024 or chunk > 2097144 for fp32       */
   KD_ERR_DTYPE = 3,     /* x_dtype / t_dtype not a kd_dtype                     */
   KD_ERR_ALIGN = 4,     /* d % 8 != 0, or a pointer not 16-byte aligned         */
   KD_ERR_WORKSPACE = 5, /* workspace_bytes < kd_chunked_workspace_size(prob)    */

@@ -161,6 +161,16 @@ def test_profile_hook_without_launches():
     assert B.kd_profile_enable(False) == 0
 
 
+def test_tile_offset_limits():
+    # 256 rows of the padded vocabulary (dZ) or of the rounded chunk (H_c^T)
+    # must stay below 2^31 bytes: the largest accepted sizes and one beyond
+    for x, vmax, cmax in ((B.KD_BF16, 4194048, 4194296), (B.KD_F32, 2097024, 2097144)):
+        assert B.kd_chunked_workspace_size(P(v=vmax, x=x, k=4, chunk=4)) > 0
+        assert B.kd_chunked_workspace_size(P(v=vmax + 1, x=x, k=4, chunk=4)) == 0
+        assert B.kd_chunked_workspace_size(P(chunk=cmax, x=x)) > 0
+        assert B.kd_chunked_workspace_size(P(chunk=cmax + 1, x=x)) == 0
+
+
 def test_temperature_zero_reads_as_one():
     assert B.kd_chunked_workspace_size(P(tau=0.0)) == B.kd_chunked_workspace_size(P(tau=1.0)) > 0
     assert B.kd_chunked_workspace_size(P(tau=0.01)) > 0 and B.kd_chunked_workspace_size(P(tau=100.0)) > 0
