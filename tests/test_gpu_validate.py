@@ -92,3 +92,17 @@ def test_bool_mask_and_last_row():
     out = L.validate_teacher(t, v, m)
     torch.cuda.synchronize()
     assert out.cpu().tolist() == [0, 0, -1, -1]
+
+
+def test_long_context_record():
+    """The 262144-row teacher record of the long-context workload (65536
+    workgroups): valid as generated; three planted faults found exactly."""
+    wl = inputs.workload("long-256k")
+    ids = inputs.make_inputs(wl, seed=0, only=("t_ids",))["t_ids"]
+    log(f"case validate long-256k n={ids.shape[0]} k={ids.shape[1]}")
+    assert _run(ids, wl.v) == (0, 0, -1, -1)
+    bad = ids.copy()
+    bad[7, 5] = wl.v
+    bad[200000, 99] = bad[200000, 0]
+    bad[262143, 50] = -1
+    assert _run(bad, wl.v) == (2, 1, 7, 200000)
