@@ -93,6 +93,27 @@ def read_traffic(path, kernel):
         return None
 
 
+def read_clock(path, kernel):
+    """Shader clock (GHz) of ``kernel`` from a committed SQ-counter summary
+    (rows ``kernel dur_ms cycles clk_GHz ...``), or None when the summary is
+    missing or was taken on other kernel sources."""
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    dig = None
+    for line in text.splitlines():
+        if line.startswith("source_digest:"):
+            dig = line.split(":", 1)[1].strip()
+        parts = line.split()
+        if len(parts) >= 4 and parts[0] == kernel and dig == source_digest():
+            try:
+                return float(parts[3])
+            except ValueError:
+                return None
+    return None
+
+
 def cpu_baseline(inp, rows_n):
     import numpy as np
 
@@ -240,6 +261,11 @@ def main():
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
                     "algorithmic_flop_per_launch": per_launch_flop, "avg_launch_ms": round(avg_s * 1e3, 4)}
+        # the rated peak assumes 2.4 GHz; the committed counter summary gives the shader clock this
+        # kernel ran at (power-limited): the same achieved rate against the peak at that clock
+        clk = read_clock(os.path.join(ROOT, "profiles", f"kd_gemms_{wl.name}_sq_counters.txt"), dom)
+        roofline["profiled_clock_ghz"] = clk
+        roofline["frac_at_profiled_clock"] = round(ach / (peak * clk / 2.4), 4) if clk else None
 
     variants = None
     if not args.no_variants:

@@ -5,7 +5,9 @@
   names the dominant kernel and was taken on the current kernel sources;
 * the source digest covers every kernel source file;
 * the projection tile width used for the memory-bound passes' byte counts is
-  the kernels' own.
+  the kernels' own;
+* the profiled clock of the dominant kernel is read only for the current
+  kernel sources.
 """
 import os
 import subprocess
@@ -52,3 +54,13 @@ def test_projection_tile_width_matches_the_kernels():
     src = open(os.path.join(ROOT, "chunked_kl_loss_row_amd", "csrc", "kd_internal.h")).read()
     m = re.search(r"constexpr int kProjBN = (\d+);", src)
     assert m and int(m.group(1)) == bench.PROJ_TILE_V
+
+
+def test_clock_read_only_for_current_sources(tmp_path):
+    p = tmp_path / "sq.txt"
+    dig = bench.source_digest()
+    p.write_text(f"# header\nsource_digest: {dig}\n# kernel dur_ms cycles clk_GHz\n  bwd_dw 2.5 4.7e6 1.932 2.4e6\n")
+    assert bench.read_clock(str(p), "bwd_dw") == 1.932
+    assert bench.read_clock(str(p), "bwd_dh") is None
+    p.write_text("source_digest: 0000000000000000\n  bwd_dw 2.5 4.7e6 1.932 2.4e6\n")
+    assert bench.read_clock(str(p), "bwd_dw") is None
