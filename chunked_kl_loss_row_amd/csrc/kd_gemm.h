@@ -236,7 +236,8 @@ struct FragReader {
   }
 };
 
-template <typename T, int BM_, int BN_, bool A_KC, bool B_KC, int WAVES_M = 2, int WAVES_N = 4, int NS_ = 4>
+template <typename T, int BM_, int BN_, bool A_KC, bool B_KC, int WAVES_M = 2, int WAVES_N = 4, int NS_ = 4,
+          bool EARLY_BARRIER = false>
 struct Gemm {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int SZ = static_cast<int>(sizeof(T));
@@ -369,11 +370,21 @@ struct Gemm {
         af[i] = read_a(cur, 1, wm, i, lane);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // The wait and barrier for tile kt+1: after the first MFMA row of step
+      // 1, or (EARLY_BARRIER) before it, where b0 is already free so the
+      // first B fragments of tile kt+1 are read one MFMA row earlier.  No
+      // fragment of tile kt is read from LDS in step 1 either way.
+      if constexpr (EARLY_BARRIER) {
+        wait_tiles(min(NS - 2, nk - kt - 2));
+        lds_barrier();
+        if (more) read_b(b0, nxt, 0, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         mma_row(acc, i, af[i], b1);
         __builtin_amdgcn_sched_barrier(0);
-        if (i == 0) {
+        if (!EARLY_BARRIER && i == 0) {
           wait_tiles(min(NS - 2, nk - kt - 2));  // tile kt+1 has landed (own loads)
           lds_barrier();                          // tile kt+1 visible; stage of kt free
           if (more) read_b(b0, nxt, 0, wn, lane);

@@ -24,9 +24,9 @@ namespace kd {
 // Block tiles: 256 x 384 (projection, dH) and 384 x 256 (dW), eight waves.
 // The projection keeps three LDS stages: its epilogue tables need the room.
 template <typename T>
-using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3>;
+using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true>;
 template <typename T>
-using DhGemm = Gemm<T, kDhBM, kDhBN, true, false>;
+using DhGemm = Gemm<T, kDhBM, kDhBN, true, false, 2, 4, 4, true>;
 template <typename T>
 using DwGemm = Gemm<T, kDwBM, kDwBN, false, true>;
 static_assert(ProjGemm<uint16_t>::NT == ProjGemm<float>::NT && DhGemm<uint16_t>::NT == DhGemm<float>::NT &&
