@@ -292,9 +292,37 @@ def main():
             "ms_per_step": round(tau_ms, 4), "tokens_per_s": round(N / (tau_ms * 1e-3), 1),
             "tflops": round(flops_step / (tau_ms * 1e-3) / 1e12, 2), "loss": float(loss.item())}}
 
+        # dW over groups of two chunks (kd_problem.dw_chunks = 2): the workspace keeps two chunks of
+        # dZ and dW is read and written once per two chunks; same flops and results as the headline
+        # (bit for bit when the chunk is a multiple of the k tile)
+        del ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        prob_g = L.make_problem(H, W, ids, lg, chunk, 1.0, 2)
+        wsg = L.workspace_for(prob_g, H.device)
+
+        def step_groups():
+            B.kd_chunked_fwd(prob_g, H, W, ids, lg, mask, loss, lse, None, None, wsg, stream=stream)
+            B.kd_chunked_bwd(prob_g, H, W, ids, lg, mask, lse, None, dH, dW, wsg, stream=stream)
+
+        step_groups()
+        torch.cuda.synchronize()
+        v0.record(stream)
+        for _ in range(vsteps):
+            step_groups()
+        v1.record(stream)
+        torch.cuda.synchronize()
+        g_ms = v0.elapsed_time(v1) / vsteps
+        variants["dw_chunks_2"] = {
+            "entry": "kd_chunked_fwd + kd_chunked_bwd, dw_chunks = 2", "steps": vsteps,
+            "ms_per_step": round(g_ms, 4), "tokens_per_s": round(N / (g_ms * 1e-3), 1),
+            "tflops": round(flops_step / (g_ms * 1e-3) / 1e12, 2),
+            "peak_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 3)}
+        del wsg
+
         # kd_chunked_fwd_bwd: the forward keeps each chunk's fp32 logits and dZ is formed from
         # them instead of recomputing the projection (6 N D V flops done; same results bit for bit)
-        del ws
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()

@@ -34,7 +34,7 @@ class KDError(RuntimeError):
 class KDProblem(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("d", ctypes.c_int32), ("v", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("chunk", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
-                ("t_dtype", ctypes.c_int32), ("tau", ctypes.c_float)]
+                ("t_dtype", ctypes.c_int32), ("tau", ctypes.c_float), ("dw_chunks", ctypes.c_int32)]
 
 
 _lib = None
@@ -102,9 +102,9 @@ def _stream(stream):
 
 
 def problem(n: int, d: int, v: int, k: int, chunk: int, x_dtype: int = KD_BF16,
-            t_dtype: Optional[int] = None, tau: float = 1.0) -> KDProblem:
+            t_dtype: Optional[int] = None, tau: float = 1.0, dw_chunks: int = 1) -> KDProblem:
     return KDProblem(int(n), int(d), int(v), int(k), int(chunk), int(x_dtype),
-                     int(x_dtype if t_dtype is None else t_dtype), float(tau))
+                     int(x_dtype if t_dtype is None else t_dtype), float(tau), int(dw_chunks))
 
 
 def kd_status_string(status: int) -> str:

@@ -41,6 +41,9 @@ struct Layout {
 
 enum class Mode { kLoss, kLossCached, kTopk };
 
+// Chunks whose dZ one dW GEMM reads (kd_problem.dw_chunks; 0 means 1).
+int dw_group(const kd_problem& p) { return p.dw_chunks > 1 ? p.dw_chunks : 1; }
+
 // kLossCached: the single-call path also keeps the chunk's fp32 logits;
 // kTopk: the teacher top-K producer (no dZ; per-row thresholds and
 // candidate lists instead).
@@ -68,10 +71,11 @@ Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   L.rl = take(C * 8);
   L.loss_acc = take(8);
   const bool loss = mode != Mode::kTopk;
-  L.dz = take(loss ? C * static_cast<size_t>(L.ldz) * xs : 0);
+  const size_t G = static_cast<size_t>(dw_group(p));
+  L.dz = take(loss ? G * C * static_cast<size_t>(L.ldz) * xs : 0);
   L.dhp = take(loss && L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
   L.zc = take(mode == Mode::kLossCached ? C * static_cast<size_t>(L.ldz) * 4 : 0);
-  L.ldt = (p.chunk + 7) / 8 * 8;
+  L.ldt = static_cast<int>((G * C + 7) / 8 * 8);
   L.ht = take(loss ? static_cast<size_t>(L.ldt) * static_cast<size_t>(p.d) * xs : 0);
   L.lmax = take(loss ? 0 : C * static_cast<size_t>(L.nvt) * kd::kTopkLanes * 4);
   L.thr = take(loss ? 0 : C * 4);
@@ -89,6 +93,7 @@ int check_problem(const kd_problem* p) {
   if (!dtype_ok(p->x_dtype) || !dtype_ok(p->t_dtype)) return KD_ERR_DTYPE;
   // temperature: 0 means 1; otherwise a finite value in [0.01, 100]
   if (!(p->tau == 0.f || (p->tau >= 0.01f && p->tau <= 100.f))) return KD_ERR_SHAPE;
+  if (p->dw_chunks < 0 || p->dw_chunks > 8) return KD_ERR_SHAPE;
   // The matrix-core tiles address a k-contiguous operand panel (256 rows of
   // its leading dimension) with 32-bit byte offsets: dZ (leading dimension
   // 384 * ceil(v / 384)) in dH and the transposed H_c (the chunk rounded up to
@@ -96,7 +101,7 @@ int check_problem(const kd_problem* p) {
   if (dtype_ok(p->x_dtype)) {
     const int64_t xs = p->x_dtype == KD_BF16 ? 2 : 4;
     const int64_t ldz = (static_cast<int64_t>(p->v) + kd::kProjBN - 1) / kd::kProjBN * kd::kProjBN;
-    const int64_t ldt = (static_cast<int64_t>(p->chunk) + 7) / 8 * 8;
+    const int64_t ldt = (static_cast<int64_t>(p->chunk) * (p->dw_chunks > 1 ? p->dw_chunks : 1) + 7) / 8 * 8;
     if (256 * ldz * xs > 0x7FFFFFF0LL || 256 * ldt * xs > 0x7FFFFFF0LL) return KD_ERR_SHAPE;
   }
   if (p->d % 8 != 0) return KD_ERR_ALIGN;
@@ -180,9 +185,21 @@ void timed(int kind, hipStream_t s, F&& launch) {
   if (a && b) g_prof_pending.push_back({kind, a, b});
 }
 
+// The dW GEMM of a group ends at chunk `a` (its last): one GEMM over the dZ
+// rows of all the group's chunks (their slots are contiguous) and the H^T
+// columns they wrote.
+void launch_group_dw(ChunkArgs a, const kd_problem& p, const Layout& L, char* base, float* dW, hipStream_t s) {
+  a.rows = a.ht_off + a.rows;  // rows of the whole group
+  a.dz = base + L.dz;
+  timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
+}
+
+// Arguments of one chunk's kernels.  `slot` is the chunk's place in its dW
+// group: its dZ goes to slot `slot` of the dZ region and its H^T to the
+// columns from slot * chunk (the chunks before it in the group are full).
 ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const void* H, const void* W,
                      const int32_t* ids, const void* logits, const uint8_t* mask, int64_t row0, int rows,
-                     bool cached = false) {
+                     bool cached = false, int slot = 0) {
   ChunkArgs a{};
   const size_t xs = p.x_dtype == KD_BF16 ? 2 : 4, ts = p.t_dtype == KD_BF16 ? 2 : 4;
   a.rows = rows;
@@ -209,13 +226,15 @@ ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const voi
   a.ps = reinterpret_cast<float*>(base + L.ps);
   a.rl = reinterpret_cast<double*>(base + L.rl);
   a.loss_acc = reinterpret_cast<double*>(base + L.loss_acc);
-  a.dz = base + L.dz;
+  a.dz = base + L.dz + static_cast<size_t>(slot) * p.chunk * static_cast<size_t>(L.ldz) * xs;
   a.dhp = reinterpret_cast<float*>(base + L.dhp);
   a.dh_split = L.split;
   a.dh_kslice = L.kslice;
   a.zc = cached ? reinterpret_cast<float*>(base + L.zc) : nullptr;
   a.ht = base + L.ht;
   a.ldt = L.ldt;
+  a.ht_off = slot * p.chunk;
+  a.ht_span = rows;
   return a;
 }
 
@@ -310,16 +329,20 @@ int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W, const i
   const Layout L = layout_for(p);
   char* base = ws_base(workspace);
   const int64_t nchunks = (p.n + p.chunk - 1) / p.chunk;
+  const int G = dw_group(p);
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t row0 = c * p.chunk;
     const int rows = static_cast<int>(p.n - row0 < p.chunk ? p.n - row0 : p.chunk);
-    const ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows);
+    const int slot = static_cast<int>(c % G);
+    const bool group_end = slot == G - 1 || c == nchunks - 1;
+    ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows, false, slot);
+    if (group_end) a.ht_span = (a.ht_off + rows + 7) / 8 * 8 - a.ht_off;
     timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
     timed(KD_K_BWD_DZ, s, [&] { kd::launch_bwd_dz(a, lse + row0, grad_loss, s); });
     timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
     if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
     timed(KD_K_H_TRANSPOSE, s, [&] { kd::launch_transpose_h(a, s); });
-    timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
+    if (group_end) launch_group_dw(a, p, L, base, dW, s);
   }
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
@@ -351,10 +374,14 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, con
   const Layout L = layout_for(p, Mode::kLossCached);
   char* base = ws_base(workspace);
   const int64_t nchunks = (p.n + p.chunk - 1) / p.chunk;
+  const int G = dw_group(p);
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t row0 = c * p.chunk;
     const int rows = static_cast<int>(p.n - row0 < p.chunk ? p.n - row0 : p.chunk);
-    const ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows, true);
+    const int slot = static_cast<int>(c % G);
+    const bool group_end = slot == G - 1 || c == nchunks - 1;
+    ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows, true, slot);
+    if (group_end) a.ht_span = (a.ht_off + rows + 7) / 8 * 8 - a.ht_off;
     timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
     timed(KD_K_FWD_PROJ, s, [&] { kd::launch_fwd_proj(a, s); });
     timed(KD_K_MERGE, s, [&] { kd::launch_merge(a, lse + row0, nullptr, nullptr, s); });
@@ -363,7 +390,7 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, con
     timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
     if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
     timed(KD_K_H_TRANSPOSE, s, [&] { kd::launch_transpose_h(a, s); });
-    timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
+    if (group_end) launch_group_dw(a, p, L, base, dW, s);
   }
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }

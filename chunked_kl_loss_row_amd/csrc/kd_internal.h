@@ -48,8 +48,10 @@ struct ChunkArgs {
   void* dz;         // [chunk][ldz] dZ in x dtype
   float* dhp;       // [split][chunk][d] split partials of dH
   float* zc;        // [chunk][ldz] fp32 logits kept by the forward (single-call path), else null
-  void* ht;         // [d][ldt] H_c transposed (x dtype), columns [rows, ldt) zero
-  int ldt;          // row stride of ht in elements (chunk rounded up to 8)
+  void* ht;         // [d][ldt] H^T of the chunks of one dW group (x dtype)
+  int ldt;          // row stride of ht in elements (dW group rows rounded up to 8)
+  int ht_off;       // column of ht where this chunk's rows start
+  int ht_span;      // columns this chunk writes from ht_off (its rows, zero-padded to 8 if last in group)
   int dh_split;     // number of V slices of the dH reduction
   int dh_kslice;    // V entries per slice (multiple of the k tile)
 };

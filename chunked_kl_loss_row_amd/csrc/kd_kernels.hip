@@ -607,12 +607,14 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
 }
 
 // H_c^T for the dW GEMM (its k = chunk row then runs contiguous in memory,
-// so both of its operands need no transposing LDS read for B).  64 x 64
-// tiles through LDS; columns [rows, ldt) are written as zeros, so a 16-byte
-// load that straddles the last row reads zeros.
+// so its B operand needs no transposing LDS read).  The chunk's rows go to
+// columns [off, off + rows) of ht; columns [off + rows, off + span) are
+// written as zeros (span rounds the last chunk of a dW group up to 8, so a
+// 16-byte load that straddles the group's last row reads zeros).  64 x 64
+// tiles through LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose_h(const T* __restrict__ Hc, int rows, int d, T* __restrict__ ht,
-                                                     int ldt) {
+                                                     int ldt, int off, int span) {
   __shared__ T tile[64][65];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;  // c: hidden column, r: chunk row
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -623,7 +625,7 @@ __global__ __launch_bounds__(256) void k_transpose_h(const T* __restrict__ Hc, i
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
-    if (c < d && r < ldt) ht[static_cast<long>(c) * ldt + r] = tile[tx][i];
+    if (c < d && r < span && off + r < ldt) ht[static_cast<long>(c) * ldt + off + r] = tile[tx][i];
   }
 }
 
@@ -1051,13 +1053,14 @@ void launch_dh_reduce(const ChunkArgs& a, float* dH, hipStream_t s) {
 }
 
 void launch_transpose_h(const ChunkArgs& a, hipStream_t s) {
-  const dim3 grid((a.d + 63) / 64, (a.ldt + 63) / 64), block(256);
+  if (a.ht_span <= 0) return;
+  const dim3 grid((a.d + 63) / 64, (a.ht_span + 63) / 64), block(256);
   if (a.x_bf16)
     k_transpose_h<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H), a.rows, a.d,
-                                                   static_cast<uint16_t*>(a.ht), a.ldt);
+                                                   static_cast<uint16_t*>(a.ht), a.ldt, a.ht_off, a.ht_span);
   else
     k_transpose_h<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), a.rows, a.d,
-                                                static_cast<float*>(a.ht), a.ldt);
+                                                static_cast<float*>(a.ht), a.ldt, a.ht_off, a.ht_span);
 }
 
 void launch_bwd_dw(const ChunkArgs& a, float* dW, hipStream_t s) {

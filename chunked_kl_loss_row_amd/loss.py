@@ -29,7 +29,8 @@ def _xdtype(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
 
 
-def make_problem(hidden, weight, t_ids, t_logits, chunk: int, temperature: float = 1.0) -> B.KDProblem:
+def make_problem(hidden, weight, t_ids, t_logits, chunk: int, temperature: float = 1.0,
+                 dw_chunks: int = 1) -> B.KDProblem:
     n, d = hidden.shape
     v, d2 = weight.shape
     if d2 != d:
@@ -40,7 +41,7 @@ def make_problem(hidden, weight, t_ids, t_logits, chunk: int, temperature: float
         raise TypeError("hidden and weight must share a dtype")
     if t_ids.dtype != torch.int32:
         raise TypeError("teacher ids must be int32")
-    return B.problem(n, d, v, t_ids.shape[1], chunk, _xdtype(hidden), _xdtype(t_logits), temperature)
+    return B.problem(n, d, v, t_ids.shape[1], chunk, _xdtype(hidden), _xdtype(t_logits), temperature, dw_chunks)
 
 
 def _check_mask(mask, n):
@@ -59,10 +60,11 @@ def workspace_for(prob: B.KDProblem, device) -> torch.Tensor:
 
 
 def forward(hidden, weight, t_ids, t_logits, mask=None, chunk: int = 2048, workspace=None,
-            row_loss: bool = False, zg: bool = False, temperature: float = 1.0) -> dict:
-    """Run kd_chunked_fwd; returns {"loss", "lse", "row_loss"?, "zg"?, "workspace"}."""
+            row_loss: bool = False, zg: bool = False, temperature: float = 1.0, dw_chunks: int = 1) -> dict:
+    """Run kd_chunked_fwd; returns {"loss", "lse", "row_loss"?, "zg"?, "workspace"}.  ``dw_chunks``
+    only sizes the workspace (it must match the backward's when the workspace is shared)."""
     _check(hidden, weight, t_ids, t_logits, mask)
-    prob = make_problem(hidden, weight, t_ids, t_logits, chunk, temperature)
+    prob = make_problem(hidden, weight, t_ids, t_logits, chunk, temperature, dw_chunks)
     _check_mask(mask, prob.n)
     dev = hidden.device
     ws = workspace if workspace is not None else workspace_for(prob, dev)
@@ -77,12 +79,13 @@ def forward(hidden, weight, t_ids, t_logits, mask=None, chunk: int = 2048, works
 
 
 def backward(hidden, weight, t_ids, t_logits, mask, lse, grad_loss=None, dW=None, chunk: int = 2048,
-             workspace=None, dH=None, temperature: float = 1.0):
+             workspace=None, dH=None, temperature: float = 1.0, dw_chunks: int = 1):
     """Run kd_chunked_bwd; returns (dH, dW).  ``dW`` (fp32) is accumulated
     into when given, else a zero buffer is made.  ``temperature`` must be the
-    forward's."""
+    forward's.  ``dw_chunks`` chunks of dZ feed one dW GEMM (more workspace,
+    fewer passes over dW)."""
     _check(hidden, weight, t_ids, t_logits, mask, lse, grad_loss)
-    prob = make_problem(hidden, weight, t_ids, t_logits, chunk, temperature)
+    prob = make_problem(hidden, weight, t_ids, t_logits, chunk, temperature, dw_chunks)
     _check_mask(mask, prob.n)
     dev = hidden.device
     ws = workspace if workspace is not None else workspace_for(prob, dev)
@@ -97,12 +100,13 @@ def backward(hidden, weight, t_ids, t_logits, mask, lse, grad_loss=None, dW=None
 
 
 def forward_backward(hidden, weight, t_ids, t_logits, mask=None, grad_loss=None, dW=None,
-                     chunk: int = 2048, workspace=None, dH=None, temperature: float = 1.0) -> dict:
+                     chunk: int = 2048, workspace=None, dH=None, temperature: float = 1.0,
+                     dw_chunks: int = 1) -> dict:
     """kd_chunked_fwd_bwd: loss, lse, dH and dW (accumulated into ``dW`` when
     given) in one call, each chunk's logits kept instead of recomputed.
     Returns {"loss", "lse", "dH", "dW", "workspace"}."""
     _check(hidden, weight, t_ids, t_logits, mask, grad_loss)
-    prob = make_problem(hidden, weight, t_ids, t_logits, chunk, temperature)
+    prob = make_problem(hidden, weight, t_ids, t_logits, chunk, temperature, dw_chunks)
     _check_mask(mask, prob.n)
     dev = hidden.device
     ws = workspace if workspace is not None else torch.empty(B.kd_chunked_fwd_bwd_workspace_size(prob),

@@ -65,9 +65,10 @@ typedef enum kd_status {
   KD_ERR_NULL = 1,      /* a required pointer is NULL                          */
   KD_ERR_SHAPE = 2,     /* n < 0, d not in [1, 65536], v < 1,
                            k not in [1, min(v,256)], chunk < 1, v > 16777215,
-                           tau neither 0 nor in [0.01, 100], or a 32-bit tile
-                           offset limit: v > 4194048 or chunk > 4194296 for
-                           bf16, v > 2097024 or chunk > 2097144 for fp32       */
+                           tau neither 0 nor in [0.01, 100], dw_chunks not in
+                           [0, 8], or a 32-bit tile offset limit: v > 4194048
+                           or chunk * max(1, dw_chunks) > 4194296 for bf16,
+                           v > 2097024 or that product > 2097144 for fp32      */
   KD_ERR_DTYPE = 3,     /* x_dtype / t_dtype not a kd_dtype                     */
   KD_ERR_ALIGN = 4,     /* d % 8 != 0, or a pointer not 16-byte aligned         */
   KD_ERR_WORKSPACE = 5, /* workspace_bytes < kd_chunked_workspace_size(prob)    */
@@ -86,6 +87,9 @@ typedef struct kd_problem {
   int32_t x_dtype; /* kd_dtype of H and W (the projection's compute dtype)      */
   int32_t t_dtype; /* kd_dtype of the teacher logits                            */
   float tau;       /* temperature: 0 or 1 = the plain loss, else in [0.01, 100]  */
+  int32_t dw_chunks; /* chunks whose dZ one dW GEMM reads, 0..8 (0 = 1): the
+                        workspace then holds that many chunks of dZ, and dW is
+                        read and written once per group instead of per chunk */
 } kd_problem;
 
 /* Bytes of workspace the fwd and bwd calls need for `prob`.  Depends on

@@ -48,8 +48,8 @@ def test_status_strings():
     assert "unknown" in B.kd_status_string(99)
 
 
-def P(n=1000, d=128, v=4096, k=16, chunk=64, x=B.KD_BF16, t=None, tau=1.0):
-    return B.problem(n, d, v, k, chunk, x, t, tau)
+def P(n=1000, d=128, v=4096, k=16, chunk=64, x=B.KD_BF16, t=None, tau=1.0, dw_chunks=1):
+    return B.problem(n, d, v, k, chunk, x, t, tau, dw_chunks)
 
 
 def test_workspace_independent_of_n():
@@ -70,7 +70,8 @@ def test_workspace_grows_with_chunk_and_dtype():
 @pytest.mark.parametrize("kw", [dict(n=-1), dict(d=0), dict(v=0), dict(k=0), dict(k=257, v=1000),
                                 dict(k=20, v=10), dict(chunk=0), dict(v=16777216),
                                 dict(d=65544), dict(tau=-1.0), dict(tau=0.005), dict(tau=101.0),
-                                dict(tau=float("nan")), dict(tau=float("inf"))])
+                                dict(tau=float("nan")), dict(tau=float("inf")), dict(dw_chunks=-1),
+                                dict(dw_chunks=9)])
 def test_bad_shapes(kw):
     prob = P(**kw)
     assert B.kd_chunked_workspace_size(prob) == 0
@@ -177,5 +178,19 @@ def test_temperature_zero_reads_as_one():
 
 
 def test_problem_struct_layout():
-    # int64 n, six int32 fields, float tau: 36 bytes padded to the int64 alignment
+    # int64 n, six int32 fields, float tau, int32 dw_chunks
     assert ctypes.sizeof(B.KDProblem) == 40 and B.KDProblem.tau.offset == 32
+    assert B.KDProblem.dw_chunks.offset == 36
+
+
+def test_dw_chunks_workspace():
+    one = B.kd_chunked_workspace_size(P(dw_chunks=1))
+    assert B.kd_chunked_workspace_size(P(dw_chunks=0)) == one
+    two = B.kd_chunked_workspace_size(P(dw_chunks=2))
+    big = B.problem(32768, 2880, 201088, 100, 2048, B.KD_BF16, None, 1.0, 2)
+    dz = 2048 * 201216 * 2  # one chunk of dZ at the gpt-oss shapes
+    assert two > one
+    assert B.kd_chunked_workspace_size(big) - B.kd_chunked_workspace_size(P(32768, 2880, 201088, 100, 2048)) >= dz
+    # the transposed H of a group also counts against the 32-bit tile limit
+    assert B.kd_chunked_workspace_size(P(chunk=2097148, dw_chunks=2)) > 0
+    assert B.kd_chunked_workspace_size(P(chunk=2097149, dw_chunks=2)) == 0
