@@ -201,6 +201,44 @@ def kd_backward(H: np.ndarray, W: np.ndarray, t_ids: np.ndarray, t_logits: np.nd
     return out
 
 
+def dw_vocab_rows(H_stored, W_stored, x_dtype: str, t_ids: np.ndarray, t_logits: np.ndarray,
+                  mask: Optional[np.ndarray], lse: np.ndarray, vocab: Sequence[int], g: float = 1.0,
+                  tau: float = 1.0, block: int = 4096) -> np.ndarray:
+    """Rows ``vocab`` (distinct ids) of ``dW`` summed over ALL positions, given
+    each row's ``lse`` (of ``z / tau`` over the full vocabulary).
+
+    The closed form of ``kd_backward`` restricted to the requested vocabulary
+    columns of dZ: ``dW_u = sum_i dZ_iu h_i`` with
+    ``dZ_iu = g tau m_i (s_i exp(z_iu / tau - lse_i) - sum_k p_ik [t_ik = u])``.
+    Because ``lse`` is given, only the requested columns of z are formed, so a
+    full-size problem fits in host memory.  ``H_stored`` / ``W_stored`` are the
+    stored inputs (``x_dtype`` as for ``widen``); H is widened block by block."""
+    vocab = np.asarray(vocab, dtype=np.int64)
+    if np.unique(vocab).size != vocab.size:
+        raise ValueError("vocab ids must be distinct")
+    n = H_stored.shape[0]
+    V = W_stored.shape[0]
+    Wv = widen(W_stored[vocab], x_dtype)                # [U, D]
+    col = np.full(V, -1, dtype=np.int64)
+    col[vocab] = np.arange(vocab.size)
+    lse = np.asarray(lse, dtype=np.float64)
+    out = np.zeros((vocab.size, Wv.shape[1]))
+    live_all = np.nonzero(_mask_rows(mask, np.arange(n)) != 0)[0]
+    for b0 in range(0, live_all.size, block):
+        live = live_all[b0:b0 + block]
+        hs = widen(H_stored[live], x_dtype)
+        z = student_logits(hs, Wv) / tau                # [r, U]
+        p, _, s = teacher_distribution(t_logits[live], tau)
+        dz = s[:, None] * np.exp(z - lse[live][:, None])
+        ids = np.asarray(t_ids[live], dtype=np.int64)
+        inside = (ids >= 0) & (ids < V)
+        j = np.where(inside, col[np.clip(ids, 0, V - 1)], -1)
+        r, kk = np.nonzero(j >= 0)
+        np.add.at(dz, (r, j[r, kk]), -p[r, kk])
+        out += (g * tau) * (dz.T @ hs)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # convenience: widen a stored input dict and run both passes
 # ----------------------------------------------------------------------------

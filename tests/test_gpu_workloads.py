@@ -3,8 +3,12 @@
 Each workload runs forward + backward over all N positions with its own chunk
 size (the launch configuration bench.py times).  The fp64 oracle cannot
 afford N x V logits at these sizes, so the checks are:
-  * sampled rows S (256 seeded positions): lse, row loss, gathered logits and
+  * sampled rows S (512 seeded positions): lse, row loss, gathered logits and
     dH rows against the oracle evaluated on exactly those rows;
+  * sampled vocabulary rows U (256 ids: half drawn from the teacher ids of
+    unmasked rows, half uniform over the vocabulary) of the full run's dW,
+    which sums over ALL N positions: the oracle forms those dZ columns from
+    the GPU's lse (already checked on S);
   * a second run with the mask restricted to S: the loss and the WHOLE dW
     (every vocab row) then come from S alone, which the oracle computes;
   * properties that hold at any size: loss = sum of row losses, L >= 0, the
@@ -25,7 +29,21 @@ from gpu_helpers import log, rel, rel_fro, upload
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-S_ROWS = 256
+S_ROWS = 512
+U_IDS = 256
+
+
+def vocab_sample(t_ids, mask, v, count, seed=0):
+    """``count`` distinct seeded vocabulary ids: half from the teacher ids of
+    unmasked rows, the rest uniform over the vocabulary (disjoint from the
+    first half)."""
+    rng = np.random.default_rng([seed, 71])
+    live = t_ids if mask is None else t_ids[mask != 0]
+    hit = np.unique(live)
+    a = rng.choice(hit, size=min(count // 2, hit.size), replace=False)
+    rest = np.setdiff1d(np.arange(v), a)
+    b = rng.choice(rest, size=count - a.size, replace=False)
+    return np.sort(np.concatenate([a, b])).astype(np.int64), a
 
 
 @pytest.mark.timeout(1200)
@@ -54,7 +72,19 @@ def test_full_workload_sampled(name):
     assert rel(loss, math.fsum(rl_all.astype(np.float64).tolist())) <= 1e-5
     col = dW.double().sum(dim=0).abs().max().item()
     assert col <= 1e-3 * dW.double().abs().sum(dim=0).max().item()
+    voc, hit = vocab_sample(inp["t_ids"], inp["mask"], wl.v, U_IDS)
+    dW_u = dW[torch.from_numpy(voc).cuda()].cpu().numpy()
+    lse_all = f["lse"].cpu().numpy()
     del dH, dW
+
+    log(f"case {name}: oracle dW on {voc.size} vocab rows over all {wl.n} positions")
+    ref_u = oracle.dw_vocab_rows(inp["H"], inp["W"], wl.x_dtype, inp["t_ids"],
+                                 oracle.widen(inp["t_logits"], wl.t_dtype), inp["mask"], lse_all, voc)
+    is_hit = np.isin(voc, hit)
+    e_hit = rel_fro(dW_u[is_hit], ref_u[is_hit])
+    e_uni = rel_fro(dW_u[~is_hit], ref_u[~is_hit])
+    log(f"case {name}: full-run dW vocab rows rel_fro hit={e_hit:.3g} uniform={e_uni:.3g}")
+    assert e_hit <= 1e-2 and e_uni <= 1e-2
 
     log(f"case {name}: oracle on {rows.size} sampled rows")
     # the oracle sees exactly the sampled positions (rows are independent)

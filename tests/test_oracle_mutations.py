@@ -5,8 +5,8 @@ dropped term, a wrong sign, a wrong index, a transposed operand, an inverted
 mask), loads the edited copy as a separate module, and runs the pins that do
 not depend on the oracle itself: the 50-digit brute-force fixture (values and
 central-difference gradients, at temperature 1 and at three other
-temperatures), the zero-loss construction and the dZ / dW sum-to-zero
-invariants.  Every mutation must fail at least one of them.
+temperatures, also for the dW rows formed from a given lse), the zero-loss
+construction and the dZ sum-to-zero invariant.  Every mutation must fail at least one of them.
 """
 import json
 import os
@@ -53,6 +53,19 @@ MUTATIONS = [
     ("gathered logit not tempered", "(p * zg_b).sum(axis=1) / tau", "(p * zg_b).sum(axis=1)"),
     ("backward logits not tempered", "z = student_logits(hs, W) / tau", "z = student_logits(hs, W)"),
     ("gradient tau factor dropped", "dz *= g * tau", "dz *= g"),
+    # dW on a subset of vocabulary rows from a given lse
+    ("vocab rows: scatter sign", "np.add.at(dz, (r, j[r, kk]), -p[r, kk])",
+     "np.add.at(dz, (r, j[r, kk]), p[r, kk])"),
+    ("vocab rows: lse ignored", "dz = s[:, None] * np.exp(z - lse[live][:, None])",
+     "dz = s[:, None] * np.exp(z)"),
+    ("vocab rows: shifted W rows", "Wv = widen(W_stored[vocab], x_dtype)",
+     "Wv = widen(W_stored[(vocab + 1) % V], x_dtype)"),
+    ("vocab rows: tau factor dropped", "out += (g * tau) * (dz.T @ hs)", "out += g * (dz.T @ hs)"),
+    ("vocab rows: mask ignored", "live_all = np.nonzero(_mask_rows(mask, np.arange(n)) != 0)[0]",
+     "live_all = np.arange(n)"),
+    ("vocab rows: column map reversed", "col[vocab] = np.arange(vocab.size)",
+     "col[vocab] = np.arange(vocab.size)[::-1]"),
+    ("vocab rows: student not tempered", "z = student_logits(hs, Wv) / tau", "z = student_logits(hs, Wv)"),
 ]
 
 
@@ -97,6 +110,10 @@ def pins(mod):
         assert np.linalg.norm(b["dH"] - dH) <= 1e-10 * np.linalg.norm(dH)
         assert np.linalg.norm(b["dW"] - dW) <= 1e-10 * np.linalg.norm(dW)
         np.testing.assert_allclose(b["dZ"].sum(axis=1), 0.0, atol=1e-13)
+        sub = np.arange(W.shape[0])[::-2]
+        dWs = mod.dw_vocab_rows(H, W, "f64", ids, a, mask, [_f(x) for x in c["lse"]], sub,
+                                g=c["g"], tau=tau, block=2)
+        assert np.linalg.norm(dWs - dW[sub]) <= 1e-10 * np.linalg.norm(dW[sub])
     # zero-loss construction
     v = d = 64
     rng = np.random.default_rng(7)

@@ -344,3 +344,59 @@ def test_temperature_one_is_the_plain_loss():
     H, W, ids, a, mask = _rand_problem()
     f, f1 = oracle.kd_forward(H, W, ids, a, mask, tau=1.0), oracle.kd_forward(H, W, ids, a, mask)
     assert f["loss"] == f1["loss"] and np.array_equal(f["lse"], f1["lse"])
+
+
+# --------------------------------------------------------------------------
+# dW on a subset of vocabulary rows, from a given lse (full-size checks)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("case", _golden(), ids=lambda c: c["name"])
+def test_dw_vocab_rows_matches_bruteforce_gradient(case):
+    """Rows of dW formed from the brute-force lse agree with the 50-digit
+    central-difference gradient, for every vocabulary row and for a subset."""
+    H, W = np.array(case["H"]), np.array(case["W"])
+    ids, a = np.array(case["t_ids"]), np.array(case["t_logits"])
+    mask = None
+    if case["masked"]:
+        mask = np.ones(case["n"], np.uint8)
+        mask[case["masked"]] = 0
+    lse = [float(mpmath.mpf(x)) for x in case["lse"]]
+    ref = _arr(case["dW"])
+    tau = case.get("tau", 1.0)
+    allv = np.arange(W.shape[0])
+    got = oracle.dw_vocab_rows(H, W, "f64", ids, a, mask, lse, allv, g=case["g"], tau=tau)
+    assert rel(got, ref) <= 1e-12
+    sub = allv[::-2]
+    got = oracle.dw_vocab_rows(H, W, "f64", ids, a, mask, lse, sub, g=case["g"], tau=tau, block=1)
+    assert rel(got, ref[sub]) <= 1e-12
+
+
+def test_dw_vocab_rows_bf16_storage_and_torch_autograd():
+    """bf16-stored inputs (uint16 bit patterns) widened block by block: the
+    selected rows equal torch fp64 autograd of the tempered loss."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(5)
+    n, d, v, k, g, tau = 23, 8, 40, 6, 0.61, 1.9
+    Hb = torch.randn(n, d).to(torch.bfloat16)
+    Wb = (0.4 * torch.randn(v, d)).to(torch.bfloat16)
+    ids = np.stack([rng.permutation(v)[:k] for _ in range(n)]).astype(np.int32)
+    ids[4, 2] = ids[4, 0]                       # a repeated id adds term by term
+    a = 2.0 * rng.standard_normal((n, k))
+    mask = (rng.random(n) > 0.25).astype(np.uint8)
+    Ht = Hb.double().requires_grad_(True)
+    Wt = Wb.double().requires_grad_(True)
+    live = torch.tensor(np.nonzero(mask)[0])
+    logq = F.log_softmax((Ht @ Wt.T) / tau, dim=1)
+    logq_t = torch.gather(logq[live], 1, torch.tensor(ids, dtype=torch.int64)[live])
+    p = torch.softmax(torch.tensor(a)[live] / tau, dim=1)
+    L = tau * tau * (p * (torch.log(p) - logq_t)).sum()
+    (g * L).backward()
+    lse = torch.logsumexp((Ht @ Wt.T) / tau, dim=1).detach().numpy()
+    hs = Hb.view(torch.int16).numpy().view(np.uint16)
+    ws = Wb.view(torch.int16).numpy().view(np.uint16)
+    sub = np.array([ids[4, 0], 0, 39, 17, ids[0, 1]])
+    sub = np.unique(sub)
+    got = oracle.dw_vocab_rows(hs, ws, "bf16", ids, a, mask, lse, sub, g=g, tau=tau, block=5)
+    assert rel(got, Wt.grad.numpy()[sub]) <= 1e-12
+    with pytest.raises(ValueError):
+        oracle.dw_vocab_rows(hs, ws, "bf16", ids, a, mask, lse, [3, 3], g=g, tau=tau)
