@@ -25,6 +25,9 @@ namespace {
 using kd::ChunkArgs;
 
 constexpr size_t kAlign = 256;
+// Projection tiles per chunk: 512 work-items each, the grid rounded up to a
+// multiple of 8, below 2^32 work-items in all.
+constexpr int64_t kMaxProjTiles = (int64_t{1} << 23) - 8;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -104,6 +107,11 @@ int check_problem(const kd_problem* p) {
     const int64_t ldt = (static_cast<int64_t>(p->chunk) * (p->dw_chunks > 1 ? p->dw_chunks : 1) + 7) / 8 * 8;
     if (256 * ldz * xs > 0x7FFFFFF0LL || 256 * ldt * xs > 0x7FFFFFF0LL) return KD_ERR_SHAPE;
   }
+  // One projection launch covers a chunk's (row tile, vocabulary tile) pairs
+  // with 512 work-items each; its work-item count must fit in 32 bits.
+  const int64_t ptiles = (static_cast<int64_t>(p->chunk) + kd::kProjBM - 1) / kd::kProjBM *
+                         ((static_cast<int64_t>(p->v) + kd::kProjBN - 1) / kd::kProjBN);
+  if (ptiles > kMaxProjTiles) return KD_ERR_SHAPE;
   if (p->d % 8 != 0) return KD_ERR_ALIGN;
   return KD_OK;
 }

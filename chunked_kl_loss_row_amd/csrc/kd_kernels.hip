@@ -611,12 +611,13 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
 // columns [off, off + rows) of ht; columns [off + rows, off + span) are
 // written as zeros (span rounds the last chunk of a dW group up to 8, so a
 // 16-byte load that straddles the group's last row reads zeros).  64 x 64
-// tiles through LDS.
+// tiles through LDS; the grid's x runs over chunk rows (a chunk may need more
+// than 65535 row tiles), y over hidden columns.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose_h(const T* __restrict__ Hc, int rows, int d, T* __restrict__ ht,
                                                      int ldt, int off, int span) {
   __shared__ T tile[64][65];
-  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;  // c: hidden column, r: chunk row
+  const int c0 = blockIdx.y * 64, r0 = blockIdx.x * 64;  // c: hidden column, r: chunk row
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int i = ty; i < 64; i += 4) {
     const int r = r0 + i, c = c0 + tx;
@@ -978,16 +979,28 @@ void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStre
 }
 
 void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s) {
-  const long threads = static_cast<long>(a.rows) * (a.ldz / 8);
-  const dim3 grid(static_cast<unsigned>((threads + 255) / 256)), block(256);
-  if (a.x_bf16)
-    k_dz_cached<uint16_t><<<grid, block, 0, s>>>(a.zc, a.ldz, a.rows, a.v, a.k, a.nvt, a.lb, a.keys, a.psort,
-                                                 a.ssum, a.mask, lse, g, static_cast<uint16_t*>(a.dz), kLog2e / a.tau,
-                                                 a.tau);
-  else
-    k_dz_cached<float><<<grid, block, 0, s>>>(a.zc, a.ldz, a.rows, a.v, a.k, a.nvt, a.lb, a.keys, a.psort,
-                                              a.ssum, a.mask, lse, g, static_cast<float*>(a.dz), kLog2e / a.tau,
-                                              a.tau);
+  // One thread per 8 columns; the chunk goes in row slices of at most 2^31
+  // threads (a launch's work-item count must fit in 32 bits).
+  const long per_row = a.ldz / 8;
+  const long slice = (1L << 31) / per_row;
+  const size_t xs = a.x_bf16 ? 2 : 4;
+  for (long r0 = 0; r0 < a.rows; r0 += slice) {
+    const int rows = static_cast<int>(a.rows - r0 < slice ? a.rows - r0 : slice);
+    const long threads = rows * per_row;
+    const dim3 grid(static_cast<unsigned>((threads + 255) / 256)), block(256);
+    const long zo = r0 * a.ldz, ko = r0 * a.k;
+    const uint16_t* lb = a.lb + r0 * (a.nvt + 1);
+    const uint8_t* mask = a.mask ? a.mask + r0 : nullptr;
+    void* dz = static_cast<char*>(a.dz) + static_cast<size_t>(zo) * xs;
+    if (a.x_bf16)
+      k_dz_cached<uint16_t><<<grid, block, 0, s>>>(a.zc + zo, a.ldz, rows, a.v, a.k, a.nvt, lb, a.keys + ko,
+                                                   a.psort + ko, a.ssum + r0, mask, lse + r0, g,
+                                                   static_cast<uint16_t*>(dz), kLog2e / a.tau, a.tau);
+    else
+      k_dz_cached<float><<<grid, block, 0, s>>>(a.zc + zo, a.ldz, rows, a.v, a.k, a.nvt, lb, a.keys + ko,
+                                                a.psort + ko, a.ssum + r0, mask, lse + r0, g,
+                                                static_cast<float*>(dz), kLog2e / a.tau, a.tau);
+  }
 }
 
 void launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s) {
@@ -1054,7 +1067,7 @@ void launch_dh_reduce(const ChunkArgs& a, float* dH, hipStream_t s) {
 
 void launch_transpose_h(const ChunkArgs& a, hipStream_t s) {
   if (a.ht_span <= 0) return;
-  const dim3 grid((a.d + 63) / 64, (a.ht_span + 63) / 64), block(256);
+  const dim3 grid((a.ht_span + 63) / 64, (a.d + 63) / 64), block(256);
   if (a.x_bf16)
     k_transpose_h<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H), a.rows, a.d,
                                                    static_cast<uint16_t*>(a.ht), a.ldt, a.ht_off, a.ht_span);

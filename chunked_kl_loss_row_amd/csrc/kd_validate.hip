@@ -14,12 +14,14 @@ __global__ __launch_bounds__(64) void k_validate_init(unsigned long long* __rest
   if (threadIdx.x < 4) out[threadIdx.x] = threadIdx.x < 2 ? 0ull : ~0ull;
 }
 
+// Rows [row0, row0 + n) of the record; ids and mask point at row 0.
 __global__ __launch_bounds__(256) void k_validate(const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask,
-                                                  long n, int K, int v, unsigned long long* __restrict__ out) {
+                                                  long row0, long n, int K, int v,
+                                                  unsigned long long* __restrict__ out) {
   __shared__ int32_t s_id[4][256];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long row = static_cast<long>(blockIdx.x) * 4 + w;
-  const bool live = row < n && (mask == nullptr || mask[row] != 0);
+  const long row = row0 + static_cast<long>(blockIdx.x) * 4 + w;
+  const bool live = row < row0 + n && (mask == nullptr || mask[row] != 0);
   int id[4];
   int out_of_range = 0;
 #pragma unroll
@@ -59,7 +61,13 @@ __global__ __launch_bounds__(256) void k_validate(const int32_t* __restrict__ id
 void launch_validate(const int32_t* ids, const uint8_t* mask, long n, int K, int v, int64_t* out, hipStream_t s) {
   unsigned long long* o = reinterpret_cast<unsigned long long*>(out);
   k_validate_init<<<1, 64, 0, s>>>(o);
-  if (n > 0) k_validate<<<static_cast<unsigned>((n + 3) / 4), 256, 0, s>>>(ids, mask, n, K, v, o);
+  // 2^24 rows (2^30 work-items) per launch: a launch's work-item count must
+  // fit in 32 bits
+  constexpr long kSlice = 1L << 24;
+  for (long r0 = 0; r0 < n; r0 += kSlice) {
+    const long rows = n - r0 < kSlice ? n - r0 : kSlice;
+    k_validate<<<static_cast<unsigned>((rows + 3) / 4), 256, 0, s>>>(ids, mask, r0, rows, K, v, o);
+  }
 }
 
 }  // namespace kd

@@ -68,7 +68,9 @@ typedef enum kd_status {
                            tau neither 0 nor in [0.01, 100], dw_chunks not in
                            [0, 8], or a 32-bit tile offset limit: v > 4194048
                            or chunk * max(1, dw_chunks) > 4194296 for bf16,
-                           v > 2097024 or that product > 2097144 for fp32      */
+                           v > 2097024 or that product > 2097144 for fp32,
+                           or more than 8388600 projection tiles per chunk:
+                           ceil(chunk / 256) * ceil(v / 384)                   */
   KD_ERR_DTYPE = 3,     /* x_dtype / t_dtype not a kd_dtype                     */
   KD_ERR_ALIGN = 4,     /* d % 8 != 0, or a pointer not 16-byte aligned         */
   KD_ERR_WORKSPACE = 5, /* workspace_bytes < kd_chunked_workspace_size(prob)    */

@@ -61,3 +61,16 @@ def rel_fro(a, b):
 
 def rel(a, b):
     return abs(a - b) / max(abs(b), 1e-300)
+
+
+def vocab_sample(t_ids, mask, v, count, seed=0):
+    """``count`` distinct seeded vocabulary ids: half from the teacher ids of
+    unmasked rows, the rest uniform over the vocabulary (disjoint from the
+    first half)."""
+    rng = np.random.default_rng([seed, 71])
+    live = t_ids if mask is None else t_ids[mask != 0]
+    hit = np.unique(live)
+    a = rng.choice(hit, size=min(count // 2, hit.size), replace=False)
+    rest = np.setdiff1d(np.arange(v), a)
+    b = rng.choice(rest, size=count - a.size, replace=False)
+    return np.sort(np.concatenate([a, b])).astype(np.int64), a

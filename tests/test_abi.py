@@ -172,6 +172,15 @@ def test_tile_offset_limits():
         assert B.kd_chunked_workspace_size(P(chunk=cmax + 1, x=x)) == 0
 
 
+def test_projection_tile_count_limit():
+    # a chunk's projection grid (512 work-items per 256 x 384 tile) must stay
+    # below 2^32 work-items: at most 8388600 tiles
+    v = 4194048                                   # 10922 vocabulary tiles
+    assert B.kd_chunked_workspace_size(P(v=v, k=4, chunk=768 * 256)) > 0          # 8388096 tiles
+    assert B.kd_chunked_workspace_size(P(v=v, k=4, chunk=768 * 256 + 1)) == 0      # 8399018 tiles
+    assert B.kd_teacher_topk_workspace_size(P(v=v, k=4, chunk=768 * 256 + 1)) == 0
+
+
 def test_temperature_zero_reads_as_one():
     assert B.kd_chunked_workspace_size(P(tau=0.0)) == B.kd_chunked_workspace_size(P(tau=1.0)) > 0
     assert B.kd_chunked_workspace_size(P(tau=0.01)) > 0 and B.kd_chunked_workspace_size(P(tau=100.0)) > 0

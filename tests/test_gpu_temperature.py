@@ -15,7 +15,7 @@ import torch
 import oracle
 from chunked_kl_loss_row_amd import inputs
 from chunked_kl_loss_row_amd import loss as L
-from gpu_helpers import dev, log, rel, rel_fro, run_hip, upload
+from gpu_helpers import dev, log, rel, rel_fro, run_hip, upload, vocab_sample
 
 pytestmark = pytest.mark.gpu
 
@@ -109,8 +109,9 @@ def test_gather_bit_exact_tempered():
 @pytest.mark.timeout(900)
 def test_gpt_oss_full_size_tempered_sampled():
     """The 32K gpt-oss workload in full at tau = 2 in the bench's launch
-    configuration, checked on 256 seeded rows (lse, row loss, dH) and, with
-    the mask restricted to those rows, the loss and the whole dW; plus the
+    configuration, checked on 512 seeded rows (lse, row loss, dH), on 256
+    vocabulary rows of the full run's dW (over all positions) and, with the
+    mask restricted to the sampled rows, the loss and the whole dW; plus the
     size-independent properties (L >= 0, loss = sum of row losses, vanishing
     vocabulary sums of dW)."""
     import math
@@ -130,12 +131,22 @@ def test_gpt_oss_full_size_tempered_sampled():
     assert loss >= 0.0 and rel(loss, math.fsum(rl_all.astype(np.float64).tolist())) <= 1e-5
     col = dW.double().sum(dim=0).abs().max().item()
     assert col <= 1e-3 * dW.double().abs().sum(dim=0).max().item()
-    rows = inputs.sample_rows(wl.n, 256, seed=3)
+    rows = inputs.sample_rows(wl.n, 512, seed=3)
     rows_t = torch.from_numpy(rows).cuda()
     lse = f["lse"][rows_t].cpu().numpy()
     dH_s = dH[rows_t].cpu().numpy()
+    voc, hit = vocab_sample(inp["t_ids"], inp["mask"], wl.v, 256, seed=3)
+    dW_u = dW[torch.from_numpy(voc).cuda()].cpu().numpy()
+    lse_all = f["lse"].cpu().numpy()
     del dH, dW
-    log("case gpt-oss tempered: oracle on 256 rows")
+    log("case gpt-oss tempered: oracle dW on 256 vocab rows over all positions")
+    ref_u = oracle.dw_vocab_rows(inp["H"], inp["W"], wl.x_dtype, inp["t_ids"],
+                                 oracle.widen(inp["t_logits"], wl.t_dtype), inp["mask"], lse_all, voc, tau=tau)
+    is_hit = np.isin(voc, hit)
+    e_hit, e_uni = rel_fro(dW_u[is_hit], ref_u[is_hit]), rel_fro(dW_u[~is_hit], ref_u[~is_hit])
+    log(f"case gpt-oss tempered: full-run dW vocab rows rel_fro hit={e_hit:.3g} uniform={e_uni:.3g}")
+    assert e_hit <= 1e-2 and e_uni <= 1e-2
+    log("case gpt-oss tempered: oracle on 512 rows")
     Hs = oracle.widen(inp["H"][rows], wl.x_dtype)
     Wx = oracle.widen(inp["W"], wl.x_dtype)
     ids_s, lg_s = inp["t_ids"][rows], oracle.widen(inp["t_logits"][rows], wl.t_dtype)

@@ -25,25 +25,13 @@ import torch
 import oracle
 from chunked_kl_loss_row_amd import inputs
 from chunked_kl_loss_row_amd import loss as L
-from gpu_helpers import log, rel, rel_fro, upload
+from gpu_helpers import log, rel, rel_fro, upload, vocab_sample
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 S_ROWS = 512
 U_IDS = 256
 
-
-def vocab_sample(t_ids, mask, v, count, seed=0):
-    """``count`` distinct seeded vocabulary ids: half from the teacher ids of
-    unmasked rows, the rest uniform over the vocabulary (disjoint from the
-    first half)."""
-    rng = np.random.default_rng([seed, 71])
-    live = t_ids if mask is None else t_ids[mask != 0]
-    hit = np.unique(live)
-    a = rng.choice(hit, size=min(count // 2, hit.size), replace=False)
-    rest = np.setdiff1d(np.arange(v), a)
-    b = rng.choice(rest, size=count - a.size, replace=False)
-    return np.sort(np.concatenate([a, b])).astype(np.int64), a
 
 
 @pytest.mark.timeout(1200)
