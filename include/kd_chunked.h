@@ -184,8 +184,8 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W,
  * Only prob->n, v and k are used (d, chunk and the dtypes are still
  * checked).  The ids of masked rows are never read.  No workspace.
  * Returns KD_OK, KD_ERR_NULL (out NULL, or t_ids NULL with n > 0),
- * KD_ERR_SHAPE, KD_ERR_ALIGN (out), KD_ERR_DEVICE or KD_ERR_LAUNCH; nothing
- * is enqueued on error. */
+ * KD_ERR_SHAPE (as for the loss calls, or n > 4 (2^31 - 1)), KD_ERR_ALIGN
+ * (out), KD_ERR_DEVICE or KD_ERR_LAUNCH; nothing is enqueued on error. */
 int kd_chunked_validate(const kd_problem* prob, const int32_t* t_ids, const uint8_t* mask,
                         int64_t* out, void* stream);
 
