@@ -22,7 +22,7 @@ KD_F32, KD_BF16 = 0, 1
 EXPORTS = ("kd_chunked_workspace_size", "kd_status_string", "kd_chunked_fwd", "kd_chunked_bwd",
            "kd_chunked_fwd_bwd_workspace_size", "kd_chunked_fwd_bwd", "kd_teacher_topk_workspace_size",
            "kd_teacher_topk", "kd_chunked_validate", "kd_profile_enable", "kd_profile_read")
-KD_K_COUNT = 14
+KD_K_COUNT = 15
 
 
 class KDError(RuntimeError):

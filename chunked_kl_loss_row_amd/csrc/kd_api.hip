@@ -36,7 +36,7 @@ bool dtype_ok(int t) { return t == KD_F32 || t == KD_BF16; }
 // Workspace regions, as byte offsets from the aligned base.
 struct Layout {
   int nvt, ldz, split, kslice;
-  size_t keys, psort, zgs, negent, ssum, lb, pm, ps, rl, loss_acc, dz, dhp, zc, ht;
+  size_t keys, psort, zgs, negent, ssum, lb, pm, ps, rl, loss_acc, dz, dhp, zc, ht, hk;
   int ldt;
   size_t lmax, thr, cnt, cand;  // teacher top-K producer
   size_t total;  // bytes from the aligned base
@@ -78,8 +78,10 @@ Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   L.dz = take(loss ? G * C * static_cast<size_t>(L.ldz) * xs : 0);
   L.dhp = take(loss && L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
   L.zc = take(mode == Mode::kLossCached ? C * static_cast<size_t>(L.ldz) * 4 : 0);
-  L.ldt = static_cast<int>((G * C + 7) / 8 * 8);
+  L.ldt = static_cast<int>((G * C + 31) / 32 * 32);  // whole k tiles of H_c^T
   L.ht = take(loss ? static_cast<size_t>(L.ldt) * static_cast<size_t>(p.d) * xs : 0);
+  // H_c in k tiles of 64 bytes (the loss projections' A operand)
+  L.hk = take(loss ? C * ((static_cast<size_t>(p.d) * xs + 63) / 64) * 64 : 0);
   L.lmax = take(loss ? 0 : C * static_cast<size_t>(L.nvt) * kd::kTopkLanes * 4);
   L.thr = take(loss ? 0 : C * 4);
   L.cnt = take(loss ? 0 : C * 4);
@@ -99,8 +101,11 @@ int check_problem(const kd_problem* p) {
   if (p->dw_chunks < 0 || p->dw_chunks > 8) return KD_ERR_SHAPE;
   // The matrix-core tiles address a k-contiguous operand panel (256 rows of
   // its leading dimension) with 32-bit byte offsets: dZ (leading dimension
-  // 384 * ceil(v / 384)) in dH and the transposed H_c (the chunk rounded up to
-  // 8) in dW must stay below 2^31 bytes per panel.
+  // 384 * ceil(v / 384)) in dH must stay below 2^31 bytes per panel.  The
+  // rows of one dW group (dw_chunks * chunk, rounded up to 8) are held to the
+  // same bound: the launch code and the kernels count group rows and the
+  // transposed H_c's row offsets in 32-bit ints, and this cap keeps them, with
+  // the rounding to whole k tiles, far from overflow.
   if (dtype_ok(p->x_dtype)) {
     const int64_t xs = p->x_dtype == KD_BF16 ? 2 : 4;
     const int64_t ldz = (static_cast<int64_t>(p->v) + kd::kProjBN - 1) / kd::kProjBN * kd::kProjBN;
@@ -152,7 +157,7 @@ int64_t g_prof_n[KD_K_COUNT];
 const char* const g_prof_names[KD_K_COUNT] = {"prep",      "fwd_proj",       "merge",         "loss_fold",
                                               "bwd_dz",    "bwd_dh",         "dh_reduce",     "bwd_dw",
                                               "dz_cached", "topk_maxima",    "topk_threshold", "topk_collect",
-                                              "topk_select", "h_transpose"};
+                                              "topk_select", "h_transpose", "h_tile"};
 
 hipEvent_t prof_event() {
   if (!g_prof_pool.empty()) {
@@ -241,6 +246,8 @@ ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const voi
   a.zc = cached ? reinterpret_cast<float*>(base + L.zc) : nullptr;
   a.ht = base + L.ht;
   a.ldt = L.ldt;
+  a.hk = base + L.hk;
+  a.ldk = p.chunk;
   a.ht_off = slot * p.chunk;
   a.ht_span = rows;
   return a;
@@ -311,6 +318,7 @@ int kd_chunked_fwd(const kd_problem* prob, const void* H, const void* W, const i
     const int rows = static_cast<int>(p.n - row0 < p.chunk ? p.n - row0 : p.chunk);
     const ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows);
     timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
+    timed(KD_K_H_TILE, s, [&] { kd::launch_tile_h(a, s); });
     timed(KD_K_FWD_PROJ, s, [&] { kd::launch_fwd_proj(a, s); });
     timed(KD_K_MERGE, s, [&] {
       kd::launch_merge(a, lse + row0, row_loss ? row_loss + row0 : nullptr, zg ? zg + row0 * p.k : nullptr, s);
@@ -344,8 +352,9 @@ int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W, const i
     const int slot = static_cast<int>(c % G);
     const bool group_end = slot == G - 1 || c == nchunks - 1;
     ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows, false, slot);
-    if (group_end) a.ht_span = (a.ht_off + rows + 7) / 8 * 8 - a.ht_off;
+    if (group_end) a.ht_span = (a.ht_off + rows + 31) / 32 * 32 - a.ht_off;
     timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
+    timed(KD_K_H_TILE, s, [&] { kd::launch_tile_h(a, s); });
     timed(KD_K_BWD_DZ, s, [&] { kd::launch_bwd_dz(a, lse + row0, grad_loss, s); });
     timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
     if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
@@ -389,8 +398,9 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, con
     const int slot = static_cast<int>(c % G);
     const bool group_end = slot == G - 1 || c == nchunks - 1;
     ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows, true, slot);
-    if (group_end) a.ht_span = (a.ht_off + rows + 7) / 8 * 8 - a.ht_off;
+    if (group_end) a.ht_span = (a.ht_off + rows + 31) / 32 * 32 - a.ht_off;
     timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
+    timed(KD_K_H_TILE, s, [&] { kd::launch_tile_h(a, s); });
     timed(KD_K_FWD_PROJ, s, [&] { kd::launch_fwd_proj(a, s); });
     timed(KD_K_MERGE, s, [&] { kd::launch_merge(a, lse + row0, nullptr, nullptr, s); });
     timed(KD_K_LOSS, s, [&] { kd::launch_loss_fold(a, c == 0, c == nchunks - 1, loss, s); });

@@ -3,9 +3,15 @@
 // C[BM x BN] (fp32, registers) = sum over a k range of A(m, k) * B(n, k).
 // Each operand is either
 //   KC  -- k contiguous in memory: element (r, k) at ptr[r * ld + k], or
-//   KO  -- k outer:                element (r, k) at ptr[k * ld + r].
-// The four contractions of the loss use: projection (KC, KC), dH = dZ W
-// (KC, KO), dW = dZ^T H (KO, KO).
+//   KO  -- k outer:                element (r, k) at ptr[k * ld + r], or
+//   KT  -- k tiled (a KC operand re-laid out by k tile): element (r, k) at
+//          ptr[(k / BK) * ld * BK + r * BK + k % BK], ld = rows per k-tile
+//          block, zero-padded in k up to a whole tile.
+// The four contractions of the loss use: projection (KT, KC), dH = dZ W
+// (KC, KO), dW = dZ^T H (KO, KT); the teacher top-K passes (KC, KC).  A KC tile reads 64 bytes of each of its
+// rows, half of each 128-byte line it touches (the other half is the next k
+// tile, fetched again one tile later); a KT tile is one contiguous block, so
+// every line it touches is read whole.
 //
 // Data movement.  Tiles go from global memory straight into LDS with
 // buffer_load ... lds (16 bytes per lane, one 1 KiB LDS block per wave
@@ -134,8 +140,9 @@ struct Operand {
   int k_lim;      // k >= k_lim reads as zero (multiple of VEC)
 };
 
-// Loads of one operand stage, R tile rows, NWAVES waves.
-template <typename T, int R, bool KC, int NWAVES>
+// Loads of one operand stage, R tile rows, NWAVES waves.  KT (with KC): the
+// operand is k tiled; the stage layout in LDS is the KC one.
+template <typename T, int R, bool KC, int NWAVES, bool KT = false>
 struct StageLoader {
   static constexpr int VEC = Elem<T>::VEC;
   static constexpr int SZ = static_cast<int>(sizeof(T));
@@ -144,6 +151,7 @@ struct StageLoader {
   static constexpr int CPR = R * SZ / 16;     // KO: 16-byte chunks per k row
   static_assert(R * 64 % (1024 * NWAVES) == 0, "stage must split evenly over the waves");
   static_assert(KC || (CPR % 16 == 0), "k-outer tiles need >= 256 bytes per k row");
+  static_assert(KC || !KT, "a k-tiled operand is k-contiguous within its tile");
 
   // byte offset from the tile's base (k part excluded for KC); kOOB when the
   // row (KC) / column chunk (KO) lies outside the operand.  kOOB plus any k
@@ -165,7 +173,8 @@ struct StageLoader {
       if (KC) {
         const int r = S >> 2, p = S & 3;
         const int c = p ^ ((r >> 2) & 3);
-        voff[i] = op.r0 + r < op.r_lim ? static_cast<uint32_t>(r * op.ld * SZ + c * 16) : kOOB;
+        const long row_bytes = KT ? 64 : op.ld * SZ;
+        voff[i] = op.r0 + r < op.r_lim ? static_cast<uint32_t>(r * row_bytes + c * 16) : kOOB;
       } else {
         const int k = S / CPR, p = S % CPR;
         const int c = p ^ fko(k);
@@ -177,6 +186,10 @@ struct StageLoader {
   // Buffer resource of the k tile starting at k0 (wave-uniform).  For a
   // k-outer tile the record stops at row k_lim, so rows past it read as zero.
   __device__ __forceinline__ u32x4 rsrc(const Operand<T>& op, int k0) const {
+    if (KT) {  // rows [r0, ld) of the block of k tile k0 / BK (64 bytes per row)
+      const long base = (static_cast<long>(k0 / BK) * op.ld + op.r0) * BK;
+      return make_rsrc(op.ptr + base, static_cast<uint64_t>(op.ld - op.r0) * 64);
+    }
     if (KC) {
       const long base = static_cast<long>(op.r0) * op.ld;
       return make_rsrc(op.ptr + base, static_cast<uint64_t>(op.extent - base) * SZ);
@@ -191,10 +204,12 @@ struct StageLoader {
   template <int I0, int I1>
   __device__ __forceinline__ void issue(const Operand<T>& op, const u32x4& rs, int k0, char* dst,
                                         int wave) const {
-    const bool kc_ok = !KC || k0 + rel_k(threadIdx.x & 63) < op.k_lim;
+    // k tiled: the buffer resource starts at the tile's block, whose k
+    // padding holds zeros
+    const bool kc_ok = !KC || KT || k0 + rel_k(threadIdx.x & 63) < op.k_lim;
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
-      const uint32_t o = KC ? voff[i] + static_cast<uint32_t>(k0 * SZ) : voff[i];
+      const uint32_t o = KC && !KT ? voff[i] + static_cast<uint32_t>(k0 * SZ) : voff[i];
       lds_dma16(rs, kc_ok ? o : kOOB, lds_addr(dst + (wave * NI + i) * 1024));
     }
   }
@@ -236,8 +251,9 @@ struct FragReader {
   }
 };
 
+// A_KT / B_KT: that operand is k tiled (KT above; requires it to be KC).
 template <typename T, int BM_, int BN_, bool A_KC, bool B_KC, int WAVES_M = 2, int WAVES_N = 4, int NS_ = 4,
-          bool EARLY_BARRIER = false>
+          bool EARLY_BARRIER = false, bool A_KT = false, bool B_KT = false>
 struct Gemm {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int SZ = static_cast<int>(sizeof(T));
@@ -252,8 +268,8 @@ struct Gemm {
   static constexpr int LDS_BYTES = NS * STAGE;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 
-  using LA = StageLoader<T, BM, A_KC, NWAVES>;
-  using LB = StageLoader<T, BN, B_KC, NWAVES>;
+  using LA = StageLoader<T, BM, A_KC, NWAVES, A_KT>;
+  using LB = StageLoader<T, BN, B_KC, NWAVES, B_KT>;
   using RA = FragReader<T, BM, A_KC>;
   using RB = FragReader<T, BN, B_KC>;
   static constexpr int NI = LA::NI + LB::NI;     // load instructions per wave per tile

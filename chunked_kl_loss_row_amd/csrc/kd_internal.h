@@ -48,8 +48,10 @@ struct ChunkArgs {
   void* dz;         // [chunk][ldz] dZ in x dtype
   float* dhp;       // [split][chunk][d] split partials of dH
   float* zc;        // [chunk][ldz] fp32 logits kept by the forward (single-call path), else null
-  void* ht;         // [d][ldt] H^T of the chunks of one dW group (x dtype)
-  int ldt;          // row stride of ht in elements (dW group rows rounded up to 8)
+  void* hk;         // H_c in k tiles of 64 bytes: [ceil(d / tile k)][ldk][tile k] (x dtype)
+  int ldk;          // rows per k-tile block of hk (the chunk size)
+  void* ht;         // H^T of the chunks of one dW group, k tiled: [ldt / tile k][d][tile k] (x dtype)
+  int ldt;          // group rows ht holds (dW group rows rounded up to 32, whole k tiles)
   int ht_off;       // column of ht where this chunk's rows start
   int ht_span;      // columns this chunk writes from ht_off (its rows, zero-padded to 8 if last in group)
   int dh_split;     // number of V slices of the dH reduction
@@ -67,6 +69,7 @@ void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStre
 void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);
 void launch_bwd_dh(const ChunkArgs& a, float* dH, hipStream_t s);
 void launch_transpose_h(const ChunkArgs& a, hipStream_t s);
+void launch_tile_h(const ChunkArgs& a, hipStream_t s);
 void launch_validate(const int32_t* ids, const uint8_t* mask, long n, int K, int v, int64_t* out, hipStream_t s);
 void launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s);
 void launch_topk_maxima(const ChunkArgs& a, uint32_t* lmax, hipStream_t s);

@@ -25,11 +25,17 @@ namespace kd {
 // The projection keeps three LDS stages: its epilogue tables need the room.
 template <typename T>
 using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true>;
+// The loss projections read H_c through its k-tiled copy (k_tile_h): every
+// 128-byte line of it a load touches is read whole.
+template <typename T>
+using ProjGemmT = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true, true>;
 template <typename T>
 using DhGemm = Gemm<T, kDhBM, kDhBN, true, false, 2, 4, 4, true>;
+// dW reads H_c^T k tiled as well (k_transpose_h writes it so).
 template <typename T>
-using DwGemm = Gemm<T, kDwBM, kDwBN, false, true>;
-static_assert(ProjGemm<uint16_t>::NT == ProjGemm<float>::NT && DhGemm<uint16_t>::NT == DhGemm<float>::NT &&
+using DwGemm = Gemm<T, kDwBM, kDwBN, false, true, 2, 4, 4, false, false, true>;
+static_assert(ProjGemm<uint16_t>::NT == ProjGemm<float>::NT && ProjGemmT<uint16_t>::NT == ProjGemm<uint16_t>::NT &&
+                  DhGemm<uint16_t>::NT == DhGemm<float>::NT &&
                   DwGemm<uint16_t>::NT == DwGemm<float>::NT,
               "one block size per kernel for both dtypes");
 
@@ -190,14 +196,14 @@ __device__ __forceinline__ void stage_slice(float* stage, const f32x16 (&acc)[G:
 // only in the single-call path (zc != null), which keeps the chunk's fp32
 // logits in the workspace for the dZ pass.
 template <typename T>
-__global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, const T* __restrict__ W,
+__global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ hk, int ldk, const T* __restrict__ W,
                                                      int rows, int d, int v, int nvt, int K,
                                                      const uint16_t* __restrict__ lb,
                                                      const uint32_t* __restrict__ keys,
                                                      float* __restrict__ zgs, float* __restrict__ pm,
                                                      float* __restrict__ ps, float* __restrict__ zc,
                                                      int ldz, float t2) {
-  using G = ProjGemm<T>;
+  using G = ProjGemmT<T>;
   __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
   __shared__ uint32_t s_hit[G::BM][kMaxHits];  // (column in tile << 8) | key slot
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ H, co
         s_hit[r][q - lo] = ((keys[static_cast<long>(gr) * K + q] >> 8) - vt * G::BN) << 8 | static_cast<uint32_t>(q);
   }
   f32x16 acc[G::FM][G::FN];
-  const Operand<T> A{H, d, static_cast<long>(rows) * d, rt * G::BM, rows, d};
+  const Operand<T> A{hk, ldk, static_cast<long>((d + G::BK - 1) / G::BK) * ldk * G::BK, rt * G::BM, rows, d};
   const Operand<T> B{W, d, static_cast<long>(v) * d, vt * G::BN, v, d};
   G::run(A, B, 0, d, smem, acc);
 
@@ -366,7 +372,7 @@ __global__ void k_zero_loss(float* loss) { loss[0] = 0.f; }
 // the teacher terms applied before the single rounding to the storage dtype.  Masked rows and columns in
 // [v, ldz) (padding of the row) are written as exact zeros.
 template <typename T>
-__global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, const T* __restrict__ W,
+__global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int ldk, const T* __restrict__ W,
                                                    int rows, int d, int v, int nvt, int K, int ldz,
                                                    const uint16_t* __restrict__ lb,
                                                    const uint32_t* __restrict__ keys,
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ gptr, T* __restrict__ dz,
                                                    float t2, float tau) {
-  using G = ProjGemm<T>;
+  using G = ProjGemmT<T>;
   __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
   __shared__ float s_lse2[G::BM], s_coef[G::BM], s_gm[G::BM];
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ H, cons
       }
   }
   f32x16 acc[G::FM][G::FN];
-  const Operand<T> A{H, d, static_cast<long>(rows) * d, rt * G::BM, rows, d};
+  const Operand<T> A{hk, ldk, static_cast<long>((d + G::BK - 1) / G::BK) * ldk * G::BK, rt * G::BM, rows, d};
   const Operand<T> B{W, d, static_cast<long>(v) * d, vt * G::BN, v, d};
   G::run(A, B, 0, d, smem, acc);
 
@@ -606,16 +612,37 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
   *reinterpret_cast<f32x4*>(dH + i4) = s;
 }
 
-// H_c^T for the dW GEMM (its k = chunk row then runs contiguous in memory,
-// so its B operand needs no transposing LDS read).  The chunk's rows go to
-// columns [off, off + rows) of ht; columns [off + rows, off + span) are
-// written as zeros (span rounds the last chunk of a dW group up to 8, so a
-// 16-byte load that straddles the group's last row reads zeros).  64 x 64
-// tiles through LDS; the grid's x runs over chunk rows (a chunk may need more
-// than 65535 row tiles), y over hidden columns.
+// H_c in k tiles for the projections: the block of k tile t holds rows
+// [0, ldk) x 64 bytes of k, element (r, k) at hk[(t ldk + r) BK + k % BK]
+// with BK = 64 / sizeof(element); k past d is written as zeros.  Rows past
+// `rows` are not written (the projections never read them).  A workgroup
+// copies two k tiles of 32 rows: eight lanes read one row's 128 bytes (whole
+// lines), and each tile's 32 rows are 2 KiB of contiguous output.  Grid: x over
+// row groups (a chunk may need more than 65535 of them), y over tile pairs.
+__global__ __launch_bounds__(256) void k_tile_h(const char* __restrict__ Hc, int rows, int row_bytes,
+                                                char* __restrict__ hk, int ldk, int nkt) {
+  const int t = threadIdx.x;
+  const int r = blockIdx.x * 32 + (t >> 3);
+  const int kt = blockIdx.y * 2 + ((t >> 2) & 1);
+  const int byte = kt * 64 + (t & 3) * 16;  // of the row
+  if (r >= rows || kt >= nkt) return;
+  uint4 x = make_uint4(0u, 0u, 0u, 0u);
+  if (byte < row_bytes) x = *reinterpret_cast<const uint4*>(Hc + static_cast<long>(r) * row_bytes + byte);
+  *reinterpret_cast<uint4*>(hk + (static_cast<long>(kt) * ldk + r) * 64 + (t & 3) * 16) = x;
+}
+
+// H_c^T for the dW GEMM, k tiled: its k (the row within the dW group) runs
+// contiguous in 64-byte tiles, element (h, q) of hidden column h and group
+// row q at ht[((q / BK) d + h) BK + q % BK], BK = 64 / sizeof(element), so the
+// B operand needs no transposing LDS read and each k tile is one block.  The
+// chunk's rows are group rows [off, off + rows); rows [off + rows, off + span)
+// are written as zeros (span rounds the last chunk of a group up to 32, a
+// whole k tile).  64 x 64 tiles through LDS; the grid's x runs over chunk rows
+// (a chunk may need more than 65535 row tiles), y over hidden columns.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose_h(const T* __restrict__ Hc, int rows, int d, T* __restrict__ ht,
                                                      int ldt, int off, int span) {
+  constexpr int BK = 64 / static_cast<int>(sizeof(T));
   __shared__ T tile[64][65];
   const int c0 = blockIdx.y * 64, r0 = blockIdx.x * 64;  // c: hidden column, r: chunk row
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -624,9 +651,11 @@ __global__ __launch_bounds__(256) void k_transpose_h(const T* __restrict__ Hc, i
     tile[i][tx] = (r < rows && c < d) ? Hc[static_cast<long>(r) * d + c] : T(0);
   }
   __syncthreads();
+  const int r = r0 + tx, q = off + r;
+  const long qo = static_cast<long>(q / BK) * d * BK + q % BK;
   for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < d && r < span && off + r < ldt) ht[static_cast<long>(c) * ldt + off + r] = tile[tx][i];
+    const int c = c0 + i;
+    if (c < d && r < span && q < ldt) ht[qo + static_cast<long>(c) * BK] = tile[tx][i];
   }
 }
 
@@ -701,7 +730,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
   const int mt = t / ntn, nt = t % ntn;
   // A(m = vocab, k = chunk row) = dZ[k][m];  B(n = hidden, k = chunk row) = H_c^T[n][k]
   const Operand<T> A{dz, ldz, static_cast<long>(rows) * ldz, mt * G::BM, ldz, rows};
-  const Operand<T> B{ht, ldt, static_cast<long>(d) * ldt, nt * G::BN, d, rows};
+  const Operand<T> B{ht, d, static_cast<long>(d) * ldt, nt * G::BN, d, rows};
   // dW += dZ^T H_c with the accumulators starting from the tile's current dW
   // values: they are loaded while the first operand tiles are in flight and
   // stored back after the last tile, so no read of dW waits after the
@@ -940,12 +969,12 @@ void launch_fwd_proj(const ChunkArgs& a, hipStream_t s) {
   const int rtn = (a.rows + kProjBM - 1) / kProjBM;
   const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
   if (a.x_bf16)
-    k_fwd_proj<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
+    k_fwd_proj<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.hk), a.ldk,
                                                 static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v,
                                                 a.nvt, a.k, a.lb, a.keys, a.zgs, a.pm, a.ps, a.zc, a.ldz,
                                                 kLog2e / a.tau);
   else
-    k_fwd_proj<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
+    k_fwd_proj<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.hk), a.ldk, static_cast<const float*>(a.W),
                                              a.rows, a.d, a.v, a.nvt, a.k, a.lb, a.keys, a.zgs, a.pm,
                                              a.ps, a.zc, a.ldz, kLog2e / a.tau);
 }
@@ -967,12 +996,12 @@ void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStre
   const int rtn = (a.rows + kProjBM - 1) / kProjBM;
   const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
   if (a.x_bf16)
-    k_bwd_dz<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
+    k_bwd_dz<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.hk), a.ldk,
                                               static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
                                               a.k, a.ldz, a.lb, a.keys, a.psort, a.ssum, a.mask, lse, g,
                                               static_cast<uint16_t*>(a.dz), kLog2e / a.tau, a.tau);
   else
-    k_bwd_dz<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
+    k_bwd_dz<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.hk), a.ldk, static_cast<const float*>(a.W),
                                            a.rows, a.d, a.v, a.nvt, a.k, a.ldz, a.lb, a.keys, a.psort,
                                            a.ssum, a.mask, lse, g, static_cast<float*>(a.dz), kLog2e / a.tau,
                                            a.tau);
@@ -1074,6 +1103,14 @@ void launch_transpose_h(const ChunkArgs& a, hipStream_t s) {
   else
     k_transpose_h<float><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), a.rows, a.d,
                                                 static_cast<float*>(a.ht), a.ldt, a.ht_off, a.ht_span);
+}
+
+void launch_tile_h(const ChunkArgs& a, hipStream_t s) {
+  const int row_bytes = a.d * (a.x_bf16 ? 2 : 4);
+  const int nkt = (row_bytes + 63) / 64;
+  const dim3 grid(static_cast<unsigned>((a.rows + 31) / 32), static_cast<unsigned>((nkt + 1) / 2)), block(256);
+  k_tile_h<<<grid, block, 0, s>>>(static_cast<const char*>(a.H), a.rows, row_bytes, static_cast<char*>(a.hk),
+                                  a.ldk, nkt);
 }
 
 void launch_bwd_dw(const ChunkArgs& a, float* dW, hipStream_t s) {

@@ -32,7 +32,8 @@ typedef enum kd_kernel_kind {
   KD_K_TOPK_COLLECT = 11,   /* top-K producer: projection + candidate collection */
   KD_K_TOPK_SELECT = 12,    /* top-K producer: per-row sort of the candidates     */
   KD_K_H_TRANSPOSE = 13,    /* backward: H_c transposed for the dW GEMM          */
-  KD_K_COUNT = 14
+  KD_K_H_TILE = 14,         /* H_c copied in k tiles for the projections         */
+  KD_K_COUNT = 15
 } kd_kernel_kind;
 
 /* Turn event recording on (1) or off (0).  Either way the accumulated
