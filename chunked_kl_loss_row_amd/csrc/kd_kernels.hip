@@ -264,10 +264,11 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ hk, i
         for (int e = 0; e < 4; ++e) mx = fmaxf(mx, x[j][e]);
       mx = group16_max(mx);
       float sm = 0.f;
+      const float mx2 = mx * t2;  // t2 = log2(e) / tau: exp((z - mx) / tau) = 2^(z t2 - mx t2)
 #pragma unroll
       for (int j = 0; j < G::BN / 64; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm += fast_exp2((x[j][e] - mx) * t2);  // t2 = log2(e) / tau
+        for (int e = 0; e < 4; ++e) sm += fast_exp2(fmaf(x[j][e], t2, -mx2));
       sm = group16_sum(sm);
       if (l16 == 0) {
         pm[static_cast<long>(grow) * nvt + vt] = mx;
