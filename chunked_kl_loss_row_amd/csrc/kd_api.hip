@@ -42,14 +42,15 @@ struct Layout {
   size_t total;  // bytes from the aligned base
 };
 
-enum class Mode { kLoss, kLossCached, kTopk };
+enum class Mode { kLoss, kLossCached, kTopk, kForward };
 
 // Chunks whose dZ one dW GEMM reads (kd_problem.dw_chunks; 0 means 1).
 int dw_group(const kd_problem& p) { return p.dw_chunks > 1 ? p.dw_chunks : 1; }
 
 // kLossCached: the single-call path also keeps the chunk's fp32 logits;
 // kTopk: the teacher top-K producer (no dZ; per-row thresholds and
-// candidate lists instead).
+// candidate lists instead); kForward: the regions kd_chunked_fwd uses (no
+// dZ, no dH partials, no H^T).
 Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   Layout L{};
   const size_t C = static_cast<size_t>(p.chunk), K = static_cast<size_t>(p.k);
@@ -74,12 +75,13 @@ Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   L.rl = take(C * 8);
   L.loss_acc = take(8);
   const bool loss = mode != Mode::kTopk;
+  const bool bwd = mode == Mode::kLoss || mode == Mode::kLossCached;
   const size_t G = static_cast<size_t>(dw_group(p));
-  L.dz = take(loss ? G * C * static_cast<size_t>(L.ldz) * xs : 0);
-  L.dhp = take(loss && L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
+  L.dz = take(bwd ? G * C * static_cast<size_t>(L.ldz) * xs : 0);
+  L.dhp = take(bwd && L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
   L.zc = take(mode == Mode::kLossCached ? C * static_cast<size_t>(L.ldz) * 4 : 0);
   L.ldt = static_cast<int>((G * C + 31) / 32 * 32);  // whole k tiles of H_c^T
-  L.ht = take(loss ? static_cast<size_t>(L.ldt) * static_cast<size_t>(p.d) * xs : 0);
+  L.ht = take(bwd ? static_cast<size_t>(L.ldt) * static_cast<size_t>(p.d) * xs : 0);
   // H_c in k tiles of 64 bytes (the loss projections' A operand)
   L.hk = take(loss ? C * ((static_cast<size_t>(p.d) * xs + 63) / 64) * 64 : 0);
   L.lmax = take(loss ? 0 : C * static_cast<size_t>(L.nvt) * kd::kTopkLanes * 4);
@@ -88,6 +90,28 @@ Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   L.cand = take(loss ? 0 : C * static_cast<size_t>(kd::kTopkCap) * 8);
   L.total = o;
   return L;
+}
+
+// Rows one kd_chunked_fwd pass covers: up to 8 chunks.  The forward keeps
+// no dZ, so its per-row regions for several chunks fit in the workspace the
+// backward needs for one; larger passes fill the chip better (fewer partly
+// filled rounds of projection tiles, fewer launches).  Every row's results
+// are computed the same way whatever the pass, and the running loss adds
+// chunk-sized slices in order, so the outputs do not depend on it.  Passes
+// stay at or below 65536 rows (one chunk if the chunk is larger).
+int fwd_pass_rows(const kd_problem& p) {
+  const size_t room = layout_for(p).total;
+  for (int g = 8; g > 1; g >>= 1) {
+    const int64_t rows = static_cast<int64_t>(g) * p.chunk;
+    if (rows > 65536) continue;
+    if (static_cast<int64_t>(g / 2) * p.chunk >= p.n) continue;  // half as many chunks cover n
+    const int64_t nvt = (static_cast<int64_t>(p.v) + kd::kProjBN - 1) / kd::kProjBN;
+    if ((rows + kd::kProjBM - 1) / kd::kProjBM * nvt > kMaxProjTiles) continue;  // the grid's limit
+    kd_problem q = p;
+    q.chunk = static_cast<int32_t>(rows);
+    if (layout_for(q, Mode::kForward).total <= room) return static_cast<int>(rows);
+  }
+  return p.chunk;
 }
 
 int check_problem(const kd_problem* p) {
@@ -310,20 +334,23 @@ int kd_chunked_fwd(const kd_problem* prob, const void* H, const void* W, const i
     kd::launch_zero_loss(loss, s);
     return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
   }
-  const Layout L = layout_for(p);
+  // passes of up to 8 chunks (fwd_pass_rows), laid out in the same workspace
+  kd_problem q = p;
+  q.chunk = fwd_pass_rows(p);
+  const Layout L = layout_for(q, Mode::kForward);
   char* base = ws_base(workspace);
-  const int64_t nchunks = (p.n + p.chunk - 1) / p.chunk;
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const int64_t row0 = c * p.chunk;
-    const int rows = static_cast<int>(p.n - row0 < p.chunk ? p.n - row0 : p.chunk);
-    const ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows);
+  const int64_t npass = (p.n + q.chunk - 1) / q.chunk;
+  for (int64_t c = 0; c < npass; ++c) {
+    const int64_t row0 = c * q.chunk;
+    const int rows = static_cast<int>(p.n - row0 < q.chunk ? p.n - row0 : q.chunk);
+    const ChunkArgs a = chunk_args(q, L, base, H, W, t_ids, t_logits, mask, row0, rows);
     timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
     timed(KD_K_H_TILE, s, [&] { kd::launch_tile_h(a, s); });
     timed(KD_K_FWD_PROJ, s, [&] { kd::launch_fwd_proj(a, s); });
     timed(KD_K_MERGE, s, [&] {
       kd::launch_merge(a, lse + row0, row_loss ? row_loss + row0 : nullptr, zg ? zg + row0 * p.k : nullptr, s);
     });
-    timed(KD_K_LOSS, s, [&] { kd::launch_loss_fold(a, c == 0, c == nchunks - 1, loss, s); });
+    timed(KD_K_LOSS, s, [&] { kd::launch_loss_fold(a, p.chunk, c == 0, c == npass - 1, loss, s); });
   }
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
@@ -403,7 +430,7 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, con
     timed(KD_K_H_TILE, s, [&] { kd::launch_tile_h(a, s); });
     timed(KD_K_FWD_PROJ, s, [&] { kd::launch_fwd_proj(a, s); });
     timed(KD_K_MERGE, s, [&] { kd::launch_merge(a, lse + row0, nullptr, nullptr, s); });
-    timed(KD_K_LOSS, s, [&] { kd::launch_loss_fold(a, c == 0, c == nchunks - 1, loss, s); });
+    timed(KD_K_LOSS, s, [&] { kd::launch_loss_fold(a, p.chunk, c == 0, c == nchunks - 1, loss, s); });
     timed(KD_K_DZ_CACHED, s, [&] { kd::launch_dz_cached(a, lse + row0, grad_loss, s); });
     timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
     if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });

@@ -63,7 +63,8 @@ int dh_split_for(int chunk, int d, int ldz, int* kslice);
 void launch_prep(const ChunkArgs& a, hipStream_t s);
 void launch_fwd_proj(const ChunkArgs& a, hipStream_t s);
 void launch_merge(const ChunkArgs& a, float* lse, float* row_loss, float* zg, hipStream_t s);
-void launch_loss_fold(const ChunkArgs& a, int first, int last, float* loss, hipStream_t s);
+// rows summed in slices of `sub` rows, each slice added to the running loss in order
+void launch_loss_fold(const ChunkArgs& a, int sub, int first, int last, float* loss, hipStream_t s);
 void launch_zero_loss(float* loss, hipStream_t s);
 void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);
 void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s);

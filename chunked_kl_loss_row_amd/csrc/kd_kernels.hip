@@ -344,20 +344,28 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ pm, con
 
 // Running loss: the chunk's row losses summed in a fixed order (fp64) and
 // folded into the accumulator; the last chunk writes the fp32 loss.
-__global__ __launch_bounds__(256) void k_loss_fold(const double* __restrict__ rl, int rows,
+__global__ __launch_bounds__(256) void k_loss_fold(const double* __restrict__ rl, int rows, int sub,
                                                    double* __restrict__ acc, int first, int last,
                                                    float* __restrict__ loss) {
+  // rows in slices of `sub` (the chunk size): each slice is summed by the
+  // same 256-way tree and added to the running loss in order, so the result
+  // does not depend on how many chunks one forward pass covers
   __shared__ double s[256];
-  double x = 0.0;
-  for (int i = threadIdx.x; i < rows; i += 256) x += rl[i];
-  s[threadIdx.x] = x;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+  double a = first ? 0.0 : acc[0];
+  for (int r0 = 0; r0 < rows; r0 += sub) {
+    const int n = min(sub, rows - r0);
+    double x = 0.0;
+    for (int i = threadIdx.x; i < n; i += 256) x += rl[r0 + i];
+    s[threadIdx.x] = x;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+      __syncthreads();
+    }
+    a += s[0];
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const double a = (first ? 0.0 : acc[0]) + s[0];
     acc[0] = a;
     if (last) loss[0] = static_cast<float>(a);
   }
@@ -987,8 +995,8 @@ void launch_merge(const ChunkArgs& a, float* lse, float* row_loss, float* zg, hi
                                                       static_cast<double>(a.tau) * static_cast<double>(a.tau));
 }
 
-void launch_loss_fold(const ChunkArgs& a, int first, int last, float* loss, hipStream_t s) {
-  k_loss_fold<<<dim3(1), dim3(256), 0, s>>>(a.rl, a.rows, a.loss_acc, first, last, loss);
+void launch_loss_fold(const ChunkArgs& a, int sub, int first, int last, float* loss, hipStream_t s) {
+  k_loss_fold<<<dim3(1), dim3(256), 0, s>>>(a.rl, a.rows, sub, a.loss_acc, first, last, loss);
 }
 
 void launch_zero_loss(float* loss, hipStream_t s) { k_zero_loss<<<dim3(1), dim3(1), 0, s>>>(loss); }

@@ -106,7 +106,11 @@ const char* kd_status_string(int status);
  * renormalises the teacher record, runs the projection H_c W^T on matrix
  * cores with an online per-row max / sum-of-exponentials and a gather of the
  * student logits at the K teacher ids, then folds the chunk into the running
- * loss.
+ * loss.  The forward keeps no dZ, so when the workspace (sized for the
+ * backward's chunk of dZ) has room it runs up to 8 consecutive chunks per
+ * pass, at most 65536 rows: each kernel launch then covers them all.  The
+ * outputs are the same bit for bit (every row is computed the same way, and
+ * the running loss adds chunk-sized slices in order).
  *   H        [n,d]  x_dtype   hidden states
  *   W        [v,d]  x_dtype   output projection (nn.Linear [out,in] layout)
  *   t_ids    [n,k]  int32     cached teacher token ids
