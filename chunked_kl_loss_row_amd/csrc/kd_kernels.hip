@@ -186,6 +186,20 @@ __device__ __forceinline__ void stage_slice(float* stage, const f32x16 (&acc)[G:
   }
 }
 
+// Tile t of a projection launch over rtn row tiles x nvt vocabulary tiles:
+// groups of 8 row tiles (2048 rows), vocabulary-major inside a group, so the
+// workgroups running together on one XCD share W panels and a few H panels in
+// its L2, however many rows the launch covers.  Up to 8 row tiles this is
+// vt = t / rtn, rt = t % rtn.
+__device__ __forceinline__ void proj_tile(int t, int rtn, int nvt, int& vt, int& rt) {
+  constexpr int RG = 8;
+  const int g = t / (RG * nvt);
+  const int gs = min(RG, rtn - g * RG);  // row tiles in this group
+  const int r = t - g * RG * nvt;
+  vt = r / gs;
+  rt = g * RG + r % gs;
+}
+
 // ---------------------------------------------------------------------------
 // forward: projection + per-tile online (max, sum exp) + top-K gather
 // ---------------------------------------------------------------------------
@@ -210,7 +224,8 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ hk, i
   const int rtn = (rows + G::BM - 1) / G::BM;
   const int t = xcd_tile(blockIdx.x, rtn * nvt);
   if (t < 0) return;
-  const int vt = t / rtn, rt = t % rtn;
+  int vt, rt;
+  proj_tile(t, rtn, nvt, vt, rt);
   const int tid = threadIdx.x;
   for (int r = tid; r < G::BM; r += G::NT) {
     const int gr = rt * G::BM + r;
