@@ -416,7 +416,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
   const int rtn = (rows + G::BM - 1) / G::BM;
   const int t = xcd_tile(blockIdx.x, rtn * nvt);
   if (t < 0) return;
-  const int vt = t / rtn, rt = t % rtn;
+  int vt, rt;
+  proj_tile(t, rtn, nvt, vt, rt);
   const int tid = threadIdx.x;
   const float g = gptr ? gptr[0] : 1.f;
   for (int r = tid; r < G::BM; r += G::NT) {
@@ -830,7 +831,8 @@ __global__ __launch_bounds__(512, 1) void k_topk_pass(const T* __restrict__ H, c
   const int rtn = (rows + G::BM - 1) / G::BM;
   const int t = xcd_tile(blockIdx.x, rtn * nvt);
   if (t < 0) return;
-  const int vt = t / rtn, rt = t % rtn;
+  int vt, rt;
+  proj_tile(t, rtn, nvt, vt, rt);
   const int tid = threadIdx.x;
   if (PASS == 1)
     for (int r = tid; r < G::BM; r += G::NT) {
