@@ -484,26 +484,6 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[jj][e] = dz_exp(x[e], coef, lse2, t2);
         }
-        // p of the row's teacher ids in this tile, subtracted before the single
-        // rounding (c: column in the tile relative to this lane's first one)
-        for (int q = 0; q < n; ++q) {
-          int c;
-          float sub;
-          if (n <= kMaxHits) {
-            c = s_hcol[row][q];
-            sub = s_hp[row][q];
-          } else {
-            const long kq = static_cast<long>(grow) * K + lo + q;
-            c = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
-            sub = psort[kq];
-          }
-          c -= l16 * 4;
-          sub *= gm;
-#pragma unroll
-          for (int jj = 0; jj < G::BN / 64; ++jj)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[jj][e] = dz_sub(o[jj][e], (c == jj * 64 + e) ? sub : 0.f);
-        }
         if (!full_tile) {  // columns past v: zero padding of dZ
 #pragma unroll
           for (int jj = 0; jj < G::BN / 64; ++jj)
@@ -520,6 +500,25 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
         } else {
           *reinterpret_cast<f32x4*>(out + c0) = f32x4{o[jj][0], o[jj][1], o[jj][2], o[jj][3]};
         }
+      }
+      // The row's teacher ids in this tile: their elements are stored again
+      // with p subtracted before the single rounding, by the lane that stored
+      // the element's group of 4 columns (same thread, same address: the
+      // second store lands last).  The other elements are unchanged, so this
+      // equals subtracting p inside the row pass.
+      for (int q = 0; q < n; ++q) {
+        int c;
+        float sub;
+        if (n <= kMaxHits) {
+          c = s_hcol[row][q];
+          sub = s_hp[row][q];
+        } else {
+          const long kq = static_cast<long>(grow) * K + lo + q;
+          c = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
+          sub = psort[kq];
+        }
+        if (((c >> 2) & 15) == l16)
+          out[c] = Elem<T>::from_f32(dz_sub(dz_exp(stage[rr * kStagePitch + c], coef, lse2, t2), sub * gm));
       }
     }
     lds_barrier();
