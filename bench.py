@@ -4,9 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path over the workload: kd_chunked_fwd
-(per chunk: teacher renormalisation, fused projection + online logsumexp +
-top-K gather, merge, running-loss fold) then kd_chunked_bwd (per chunk:
-recomputed projection + closed-form dZ, dH = dZ W, dW += dZ^T H).  Inputs are
+(per pass of up to 8 chunks: teacher renormalisation, fused projection +
+online logsumexp + top-K gather, merge, running-loss fold) then
+kd_chunked_bwd (per chunk: recomputed projection + closed-form dZ,
+dH = dZ W, dW += dZ^T H).  Inputs are
 seeded synthetic tensors already resident in HBM when timing starts; dW keeps
 accumulating across steps (it is zeroed once, outside the timed region).
 
