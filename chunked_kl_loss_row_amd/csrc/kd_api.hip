@@ -82,8 +82,8 @@ Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   L.zc = take(mode == Mode::kLossCached ? C * static_cast<size_t>(L.ldz) * 4 : 0);
   L.ldt = static_cast<int>((G * C + 31) / 32 * 32);  // whole k tiles of H_c^T
   L.ht = take(bwd ? static_cast<size_t>(L.ldt) * static_cast<size_t>(p.d) * xs : 0);
-  // H_c in k tiles of 64 bytes (the loss projections' A operand)
-  L.hk = take(loss ? C * ((static_cast<size_t>(p.d) * xs + 63) / 64) * 64 : 0);
+  // H_c in k tiles of 64 bytes (the A operand of every projection)
+  L.hk = take(C * ((static_cast<size_t>(p.d) * xs + 63) / 64) * 64);
   L.lmax = take(loss ? 0 : C * static_cast<size_t>(L.nvt) * kd::kTopkLanes * 4);
   L.thr = take(loss ? 0 : C * 4);
   L.cnt = take(loss ? 0 : C * 4);
@@ -472,6 +472,7 @@ int kd_teacher_topk(const kd_problem* prob, const void* H, const void* W, int32_
     ChunkArgs a = chunk_args(p, L, base, H, W, nullptr, nullptr, nullptr, 0, rows);
     const size_t xs = p.x_dtype == KD_BF16 ? 2 : 4;
     a.H = static_cast<const char*>(H) + static_cast<size_t>(row0) * p.d * xs;
+    timed(KD_K_H_TILE, s, [&] { kd::launch_tile_h(a, s); });
     timed(KD_K_TOPK_MAXIMA, s, [&] { kd::launch_topk_maxima(a, lmax, s); });
     timed(KD_K_TOPK_THRESHOLD, s, [&] { kd::launch_topk_threshold(a, lmax, thr, cnt, s); });
     timed(KD_K_TOPK_COLLECT, s, [&] { kd::launch_topk_collect(a, thr, cnt, cand, s); });

@@ -820,11 +820,11 @@ __global__ __launch_bounds__(256) void k_topk_threshold(const uint32_t* __restri
 // list (one atomic add per row and tile with candidates; a list longer than
 // kTopkCap keeps kTopkCap entries and the select pass reports the row).
 template <typename T, int PASS>
-__global__ __launch_bounds__(512, 1) void k_topk_pass(const T* __restrict__ H, const T* __restrict__ W, int rows,
+__global__ __launch_bounds__(512, 1) void k_topk_pass(const T* __restrict__ hk, int ldk, const T* __restrict__ W, int rows,
                                                       int d, int v, int nvt, uint32_t* __restrict__ lmax,
                                                       const uint32_t* __restrict__ thr, int* __restrict__ cnt,
                                                       uint64_t* __restrict__ cand) {
-  using G = ProjGemm<T>;
+  using G = ProjGemmT<T>;  // H_c through its k-tiled copy
   __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
   __shared__ uint32_t s_thr[G::BM];
   const int rtn = (rows + G::BM - 1) / G::BM;
@@ -839,7 +839,7 @@ __global__ __launch_bounds__(512, 1) void k_topk_pass(const T* __restrict__ H, c
       s_thr[r] = gr < rows ? thr[gr] : 0xFFFFFFFFu;
     }
   f32x16 acc[G::FM][G::FN];
-  const Operand<T> A{H, d, static_cast<long>(rows) * d, rt * G::BM, rows, d};
+  const Operand<T> A{hk, ldk, static_cast<long>((d + G::BK - 1) / G::BK) * ldk * G::BK, rt * G::BM, rows, d};
   const Operand<T> B{W, d, static_cast<long>(v) * d, vt * G::BN, v, d};
   G::run(A, B, 0, d, smem, acc);
 
@@ -1066,11 +1066,11 @@ void launch_topk_maxima(const ChunkArgs& a, uint32_t* lmax, hipStream_t s) {
   const int rtn = (a.rows + kProjBM - 1) / kProjBM;
   const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
   if (a.x_bf16)
-    k_topk_pass<uint16_t, 0><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
+    k_topk_pass<uint16_t, 0><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.hk), a.ldk,
                                                     static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
                                                     lmax, nullptr, nullptr, nullptr);
   else
-    k_topk_pass<float, 0><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
+    k_topk_pass<float, 0><<<grid, block, 0, s>>>(static_cast<const float*>(a.hk), a.ldk, static_cast<const float*>(a.W),
                                                  a.rows, a.d, a.v, a.nvt, lmax, nullptr, nullptr, nullptr);
 }
 
@@ -1082,11 +1082,11 @@ void launch_topk_collect(const ChunkArgs& a, const uint32_t* thr, int* cnt, uint
   const int rtn = (a.rows + kProjBM - 1) / kProjBM;
   const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
   if (a.x_bf16)
-    k_topk_pass<uint16_t, 1><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.H),
+    k_topk_pass<uint16_t, 1><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.hk), a.ldk,
                                                     static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
                                                     nullptr, thr, cnt, cand);
   else
-    k_topk_pass<float, 1><<<grid, block, 0, s>>>(static_cast<const float*>(a.H), static_cast<const float*>(a.W),
+    k_topk_pass<float, 1><<<grid, block, 0, s>>>(static_cast<const float*>(a.hk), a.ldk, static_cast<const float*>(a.W),
                                                  a.rows, a.d, a.v, a.nvt, nullptr, thr, cnt, cand);
 }
 
