@@ -32,8 +32,10 @@ extern "C" {
 
 /* Bytes of workspace kd_teacher_topk needs: per chunk 16 sampled maxima per
  * row and vocabulary tile, a threshold and a list of up to 8192 candidate
- * logits per row (8 bytes each).  Uses d, v, k, chunk and x_dtype of `prob` (t_dtype is ignored);
- * independent of n.  Returns 0 for an invalid problem. */
+ * logits per row (8 bytes each), and the chunk's hidden states copied in
+ * k tiles for the projection passes.  Uses d, v, k, chunk and x_dtype of
+ * `prob` (t_dtype is ignored); independent of n.  Returns 0 for an invalid
+ * problem. */
 size_t kd_teacher_topk_workspace_size(const kd_problem* prob);
 
 /* Teacher top-K record.
