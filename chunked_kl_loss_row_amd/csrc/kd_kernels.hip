@@ -53,13 +53,17 @@ constexpr int proj_smem_bytes() { return G::LDS_BYTES > kStageBytes ? G::LDS_BYT
 // the temperature (the top-K record renormalised over its entries);
 // negent = sum p log p; s = sum p.
 // keys = (id << 8 | k) sorted ascending with p / zg slots in the same order;
-// lb[t] = index of the first key whose id lies in vocabulary tile >= t, so
-// the keys falling in tile t are [lb[t], lb[t+1]).  Masked rows read
-// nothing and get empty ranges.
+// an id outside [0, v) takes the id field 0xFFFFFF, which no vocabulary
+// entry has (v <= 0xFFFFFF) and which lies past every tile, so it matches
+// nothing (the 24-bit field would otherwise alias ids >= 2^24 and negative
+// ids onto vocabulary entries).  lb[t] = index of the first key whose id
+// lies in vocabulary tile >= t, so the keys falling in tile t are
+// [lb[t], lb[t+1]).  Masked rows read nothing and get empty ranges.
+constexpr uint32_t kNoId = 0xFFFFFFu;
 template <typename TT>
 __global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
                                               const TT* __restrict__ logits,
-                                              const uint8_t* __restrict__ mask, int rows, int K,
+                                              const uint8_t* __restrict__ mask, int rows, int K, int v,
                                               int nvt, float inv_tau, uint32_t* __restrict__ keys,
                                               float* __restrict__ psort, float* __restrict__ zgs,
                                               float* __restrict__ negent, float* __restrict__ ssum,
@@ -87,7 +91,8 @@ __global__ __launch_bounds__(256) void k_prep(const int32_t* __restrict__ ids,
       const int k = lane + 64 * q;
       a[q] = -INFINITY;
       if (k < K) {
-        key[q] = (static_cast<uint32_t>(ids[rbase + k]) << 8) | static_cast<uint32_t>(k);
+        const uint32_t id = static_cast<uint32_t>(ids[rbase + k]);
+        key[q] = ((id < static_cast<uint32_t>(v) ? id : kNoId) << 8) | static_cast<uint32_t>(k);
         a[q] = Elem<TT>::to_f32(logits[rbase + k]);
         amax = fmaxf(amax, a[q]);
       }
@@ -504,8 +509,14 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
       // The row's teacher ids in this tile: their elements are stored again
       // with p subtracted before the single rounding, by the lane that stored
       // the element's group of 4 columns (same thread, same address: the
-      // second store lands last).  The other elements are unchanged, so this
-      // equals subtracting p inside the row pass.
+      // later store lands last).  The keys are sorted by id, so the hits of
+      // an id that repeats in the row are adjacent: the owning lane carries
+      // one fp32 value per column, subtracts each p from it in key order
+      // (the order of the cached-logit pass) and stores it after each hit,
+      // so the last store of a column holds every term.  The other elements
+      // are unchanged, so this equals subtracting p inside the row pass.
+      int prev_c = -1;
+      float run = 0.f;
       for (int q = 0; q < n; ++q) {
         int c;
         float sub;
@@ -517,8 +528,12 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
           c = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
           sub = psort[kq];
         }
-        if (((c >> 2) & 15) == l16)
-          out[c] = Elem<T>::from_f32(dz_sub(dz_exp(stage[rr * kStagePitch + c], coef, lse2, t2), sub * gm));
+        if (((c >> 2) & 15) == l16) {
+          if (c != prev_c) run = dz_exp(stage[rr * kStagePitch + c], coef, lse2, t2);
+          run = dz_sub(run, sub * gm);
+          out[c] = Elem<T>::from_f32(run);
+        }
+        prev_c = c;
       }
     }
     lds_barrier();
@@ -983,11 +998,11 @@ void launch_prep(const ChunkArgs& a, hipStream_t s) {
   const dim3 grid((a.rows + 3) / 4), block(256);
   if (a.t_bf16)
     k_prep<uint16_t><<<grid, block, 0, s>>>(a.ids, static_cast<const uint16_t*>(a.logits), a.mask, a.rows,
-                                            a.k, a.nvt, 1.0f / a.tau, a.keys, a.psort, a.zgs, a.negent,
+                                            a.k, a.v, a.nvt, 1.0f / a.tau, a.keys, a.psort, a.zgs, a.negent,
                                             a.ssum, a.lb);
   else
     k_prep<float><<<grid, block, 0, s>>>(a.ids, static_cast<const float*>(a.logits), a.mask, a.rows, a.k,
-                                         a.nvt, 1.0f / a.tau, a.keys, a.psort, a.zgs, a.negent, a.ssum, a.lb);
+                                         a.v, a.nvt, 1.0f / a.tau, a.keys, a.psort, a.zgs, a.negent, a.ssum, a.lb);
 }
 
 void launch_fwd_proj(const ChunkArgs& a, hipStream_t s) {
