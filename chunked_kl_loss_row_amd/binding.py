@@ -21,7 +21,9 @@ KD_F32, KD_BF16 = 0, 1
 # names declared by include/kd_chunked.h and include/kd_profile.h
 EXPORTS = ("kd_chunked_workspace_size", "kd_status_string", "kd_chunked_fwd", "kd_chunked_bwd",
            "kd_chunked_fwd_bwd_workspace_size", "kd_chunked_fwd_bwd", "kd_teacher_topk_workspace_size",
-           "kd_teacher_topk", "kd_chunked_validate", "kd_profile_enable", "kd_profile_read")
+           "kd_teacher_topk", "kd_chunked_validate", "kd_profile_enable", "kd_profile_read",
+           "kd_chunked_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KD_NOALLOC_SCRATCH_BYTES of include/kd_chunked.h
 KD_K_COUNT = 15
 
 
@@ -55,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.kd_status_string.restype = ctypes.c_char_p
         L.kd_chunked_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.kd_chunked_fwd.restype = ctypes.c_int
+        L.kd_chunked_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.kd_chunked_fwd_noalloc.restype = ctypes.c_int
         L.kd_chunked_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.kd_chunked_bwd.restype = ctypes.c_int
         L.kd_chunked_fwd_bwd_workspace_size.argtypes = [P]
@@ -126,6 +130,18 @@ def kd_chunked_fwd(prob: KDProblem, H, W, t_ids, t_logits, mask, loss, lse, row_
                               _ptr(workspace), wsb, _stream(stream))
     if check and st != KD_OK:
         raise KDError(st, "kd_chunked_fwd")
+    return st
+
+
+def kd_chunked_fwd_noalloc(prob: KDProblem, H, W, t_ids, t_logits, mask, loss, lse, row_loss=None, zg=None,
+                           stream=None, check: bool = True) -> int:
+    """Enqueue the forward with the library's own device scratch instead of a
+    workspace (see include/kd_chunked.h); allocates nothing."""
+    st = lib().kd_chunked_fwd_noalloc(ctypes.byref(prob), _ptr(H), _ptr(W), _ptr(t_ids), _ptr(t_logits),
+                                      _ptr(mask), _ptr(loss), _ptr(lse), _ptr(row_loss), _ptr(zg),
+                                      _stream(stream))
+    if check and st != KD_OK:
+        raise KDError(st, "kd_chunked_fwd_noalloc")
     return st
 
 

@@ -99,8 +99,7 @@ Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
 // are computed the same way whatever the pass, and the running loss adds
 // chunk-sized slices in order, so the outputs do not depend on it.  Passes
 // stay at or below 65536 rows (one chunk if the chunk is larger).
-int fwd_pass_rows(const kd_problem& p) {
-  const size_t room = layout_for(p).total;
+int fwd_pass_rows(const kd_problem& p, size_t room) {
   for (int g = 8; g > 1; g >>= 1) {
     const int64_t rows = static_cast<int64_t>(g) * p.chunk;
     if (rows > 65536) continue;
@@ -277,6 +276,53 @@ ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const voi
   return a;
 }
 
+// ---- scratch of kd_chunked_fwd_noalloc ----
+// File-scope device array standing in for the caller's workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not the device array: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is passed to kernels.
+constexpr size_t kScratchBytes = KD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[256];  // per device, null until looked up
+
+int scratch_for_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return KD_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return KD_ERR_LAUNCH;
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return KD_OK;
+}
+
+// The forward's chunk walk in passes of `pass_rows` rows (a multiple of the
+// chunk, or the chunk), with the kForward layout of one pass at `base`.
+void forward_passes(const kd_problem& p, int pass_rows, const void* H, const void* W, const int32_t* t_ids,
+                    const void* t_logits, const uint8_t* mask, float* loss, float* lse, float* row_loss,
+                    float* zg, char* base, hipStream_t s) {
+  kd_problem q = p;
+  q.chunk = pass_rows;
+  const Layout L = layout_for(q, Mode::kForward);
+  const int64_t npass = (p.n + q.chunk - 1) / q.chunk;
+  for (int64_t c = 0; c < npass; ++c) {
+    const int64_t row0 = c * q.chunk;
+    const int rows = static_cast<int>(p.n - row0 < q.chunk ? p.n - row0 : q.chunk);
+    const ChunkArgs a = chunk_args(q, L, base, H, W, t_ids, t_logits, mask, row0, rows);
+    timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
+    timed(KD_K_H_TILE, s, [&] { kd::launch_tile_h(a, s); });
+    timed(KD_K_FWD_PROJ, s, [&] { kd::launch_fwd_proj(a, s); });
+    timed(KD_K_MERGE, s, [&] {
+      kd::launch_merge(a, lse + row0, row_loss ? row_loss + row0 : nullptr, zg ? zg + row0 * p.k : nullptr, s);
+    });
+    timed(KD_K_LOSS, s, [&] { kd::launch_loss_fold(a, p.chunk, c == 0, c == npass - 1, loss, s); });
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -335,23 +381,37 @@ int kd_chunked_fwd(const kd_problem* prob, const void* H, const void* W, const i
     return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
   }
   // passes of up to 8 chunks (fwd_pass_rows), laid out in the same workspace
-  kd_problem q = p;
-  q.chunk = fwd_pass_rows(p);
-  const Layout L = layout_for(q, Mode::kForward);
-  char* base = ws_base(workspace);
-  const int64_t npass = (p.n + q.chunk - 1) / q.chunk;
-  for (int64_t c = 0; c < npass; ++c) {
-    const int64_t row0 = c * q.chunk;
-    const int rows = static_cast<int>(p.n - row0 < q.chunk ? p.n - row0 : q.chunk);
-    const ChunkArgs a = chunk_args(q, L, base, H, W, t_ids, t_logits, mask, row0, rows);
-    timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
-    timed(KD_K_H_TILE, s, [&] { kd::launch_tile_h(a, s); });
-    timed(KD_K_FWD_PROJ, s, [&] { kd::launch_fwd_proj(a, s); });
-    timed(KD_K_MERGE, s, [&] {
-      kd::launch_merge(a, lse + row0, row_loss ? row_loss + row0 : nullptr, zg ? zg + row0 * p.k : nullptr, s);
-    });
-    timed(KD_K_LOSS, s, [&] { kd::launch_loss_fold(a, p.chunk, c == 0, c == npass - 1, loss, s); });
+  forward_passes(p, fwd_pass_rows(p, layout_for(p).total), H, W, t_ids, t_logits, mask, loss, lse, row_loss, zg,
+                 ws_base(workspace), s);
+  return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
+}
+
+int kd_chunked_fwd_noalloc(const kd_problem* prob, const void* H, const void* W, const int32_t* t_ids,
+                           const void* t_logits, const uint8_t* mask, float* loss, float* lse, float* row_loss,
+                           float* zg, void* stream) {
+  int st = check_problem(prob);
+  if (st != KD_OK) return st;
+  const kd_problem& p = *prob;
+  if (!loss) return KD_ERR_NULL;
+  if (p.n > 0 && (!H || !W || !t_ids || !t_logits || !lse)) return KD_ERR_NULL;
+  if (p.n > 0 && (!aligned16(H) || !aligned16(W))) return KD_ERR_ALIGN;
+  if (layout_for(p, Mode::kForward).total > kScratchBytes) return KD_ERR_WORKSPACE;
+  st = check_device();
+  if (st != KD_OK) return st;
+  char* base = nullptr;
+  st = scratch_for_current_device(&base);
+  if (st != KD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (p.n == 0) {
+    kd::launch_zero_loss(loss, s);
+    return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
   }
+  // Nothing in the scratch must start at zero: every region the forward
+  // reads is written earlier in the same pass (the running loss starts from
+  // 0 in the first pass), so what an earlier call left there is never read.
+  forward_passes(p, fwd_pass_rows(p, kScratchBytes), H, W, t_ids, t_logits, mask, loss, lse, row_loss, zg, base,
+                 s);
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }
 

@@ -173,6 +173,34 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W,
                        const float* grad_loss, float* loss, float* lse, float* dH, float* dW,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device scratch kd_chunked_fwd_noalloc holds per GPU. */
+#define KD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* Forward without allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same computation, arguments and results as kd_chunked_fwd
+ * (loss, lse, row_loss and zg bit for bit), but the chunk workspace is a
+ * file-scope device array of KD_NOALLOC_SCRATCH_BYTES inside the library
+ * instead of a caller buffer; the call allocates and frees nothing.
+ *  - Limit: one chunk's forward regions must fit the array, about
+ *      chunk * (12 k + 10 ceil(v / 384) + 64 ceil(d x / 64) + 18) bytes
+ *    (x = 2 for bf16, 4 for fp32), plus up to 256 bytes for each of its 11
+ *    regions' alignment, e.g.
+ *    chunk 2048 at d = 2880, v = 201088, k = 100, bf16: 25 MB.  A larger
+ *    problem returns KD_ERR_WORKSPACE and enqueues nothing; pick a smaller
+ *    chunk.  Consecutive chunks share a pass (one launch per kernel) when
+ *    they fit together.
+ *  - Each GPU has one such array, shared by every call on it; it keeps the
+ *    last call's contents, none of which a later call reads.  Calls that
+ *    overlap on one GPU (other streams, other host threads) race on it:
+ *    serialise them.
+ *  - The first call on a device looks up the array's device address
+ *    (hipGetSymbolAddress); make that call before any graph capture.
+ * Returns KD_OK or an error status (nothing enqueued on error). */
+int kd_chunked_fwd_noalloc(const kd_problem* prob, const void* H, const void* W,
+                           const int32_t* t_ids, const void* t_logits, const uint8_t* mask,
+                           float* loss, float* lse, float* row_loss, float* zg, void* stream);
+
 /* Debug check of the teacher record against what the loss assumes of it.
  * The cache holds, per position, the K most probable teacher tokens
  * (agentlenshq.com page, section "1. Top-K Logit Cachingによるオフライン

@@ -203,3 +203,38 @@ def test_dw_chunks_workspace():
     # the transposed H of a group also counts against the 32-bit tile limit
     assert B.kd_chunked_workspace_size(P(chunk=2097148, dw_chunks=2)) > 0
     assert B.kd_chunked_workspace_size(P(chunk=2097149, dw_chunks=2)) == 0
+
+
+def test_noalloc_forward_argument_errors():
+    """kd_chunked_fwd_noalloc checks its arguments like kd_chunked_fwd, and
+    refuses a problem whose chunk does not fit the library's scratch."""
+    fake = 1 << 20
+    lib = B.lib()
+    assert lib.kd_chunked_fwd_noalloc(None, fake, fake, fake, fake, None, fake, fake, None, None, None) == \
+        B.KD_ERR_NULL
+    assert B.kd_chunked_fwd_noalloc(P(k=0), fake, fake, fake, fake, None, fake, fake, stream=0,
+                                    check=False) == B.KD_ERR_SHAPE
+    assert B.kd_chunked_fwd_noalloc(P(), fake, fake, fake, fake, None, None, fake, stream=0,
+                                    check=False) == B.KD_ERR_NULL
+    assert B.kd_chunked_fwd_noalloc(P(), fake, None, fake, fake, None, fake, fake, stream=0,
+                                    check=False) == B.KD_ERR_NULL
+    assert B.kd_chunked_fwd_noalloc(P(), fake + 8, fake, fake, fake, None, fake, fake, stream=0,
+                                    check=False) == B.KD_ERR_ALIGN
+    # one 2048-row chunk of the 32K gpt-oss shapes fits (about 25 MB); 8192 rows do not
+    big = dict(n=32768, d=2880, v=201088, k=100)
+    st_fit = B.kd_chunked_fwd_noalloc(P(chunk=2048, **big), fake, fake, fake, fake, None, fake, fake,
+                                      stream=0, check=False)
+    assert st_fit != B.KD_ERR_WORKSPACE
+    assert B.kd_chunked_fwd_noalloc(P(chunk=8192, **big), fake, fake, fake, fake, None, fake, fake,
+                                    stream=0, check=False) == B.KD_ERR_WORKSPACE
+    if not _has_gpu():
+        assert st_fit == B.KD_ERR_DEVICE
+    # the oversized problem the GPU test uses is refused on the host
+    assert B.kd_chunked_fwd_noalloc(B.problem(64, 8192, 200000, 100, 4096, B.KD_BF16), fake, fake, fake, fake,
+                                    None, fake, fake, stream=0, check=False) == B.KD_ERR_WORKSPACE
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "kd_chunked.h")).read()
+    m = re.search(r"#define KD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
