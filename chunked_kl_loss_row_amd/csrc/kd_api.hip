@@ -36,6 +36,7 @@ bool dtype_ok(int t) { return t == KD_F32 || t == KD_BF16; }
 // Workspace regions, as byte offsets from the aligned base.
 struct Layout {
   int nvt, ldz, split, kslice;
+  int rows;  // row capacity of the per-row regions (one backward unit: a group of chunks)
   size_t keys, psort, zgs, negent, ssum, lb, pm, ps, rl, loss_acc, dz, dhp, zc, ht, hk;
   int ldt;
   size_t lmax, thr, cnt, cand;  // teacher top-K producer
@@ -51,9 +52,16 @@ int dw_group(const kd_problem& p) { return p.dw_chunks > 1 ? p.dw_chunks : 1; }
 // kTopk: the teacher top-K producer (no dZ; per-row thresholds and
 // candidate lists instead); kForward: the regions kd_chunked_fwd uses (no
 // dZ, no dH partials, no H^T).
+// The backward walks groups of dw_chunks chunks (one launch of each kernel per
+// group), so in the backward modes every per-row region holds a group's rows.
+// The dH split stays that of one chunk: each row's dH is then summed over the
+// same V slices in the same order whatever the grouping.
 Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   Layout L{};
-  const size_t C = static_cast<size_t>(p.chunk), K = static_cast<size_t>(p.k);
+  const bool bwd = mode == Mode::kLoss || mode == Mode::kLossCached;
+  const size_t G = static_cast<size_t>(dw_group(p));
+  const size_t C = static_cast<size_t>(p.chunk) * (bwd ? G : 1), K = static_cast<size_t>(p.k);
+  L.rows = static_cast<int>(C);
   L.nvt = (p.v + kd::kProjBN - 1) / kd::kProjBN;
   L.ldz = L.nvt * kd::kProjBN;
   L.split = kd::dh_split_for(p.chunk, p.d, L.ldz, &L.kslice);
@@ -75,12 +83,11 @@ Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   L.rl = take(C * 8);
   L.loss_acc = take(8);
   const bool loss = mode != Mode::kTopk;
-  const bool bwd = mode == Mode::kLoss || mode == Mode::kLossCached;
-  const size_t G = static_cast<size_t>(dw_group(p));
-  L.dz = take(bwd ? G * C * static_cast<size_t>(L.ldz) * xs : 0);
+  L.dz = take(bwd ? C * static_cast<size_t>(L.ldz) * xs : 0);
   L.dhp = take(bwd && L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
-  L.zc = take(mode == Mode::kLossCached ? C * static_cast<size_t>(L.ldz) * 4 : 0);
-  L.ldt = static_cast<int>((G * C + 31) / 32 * 32);  // whole k tiles of H_c^T
+  // the single-call path keeps one chunk of fp32 logits at a time
+  L.zc = take(mode == Mode::kLossCached ? static_cast<size_t>(p.chunk) * static_cast<size_t>(L.ldz) * 4 : 0);
+  L.ldt = static_cast<int>((C + 31) / 32 * 32);  // whole k tiles of H_c^T
   L.ht = take(bwd ? static_cast<size_t>(L.ldt) * static_cast<size_t>(p.d) * xs : 0);
   // H_c in k tiles of 64 bytes (the A operand of every projection)
   L.hk = take(C * ((static_cast<size_t>(p.d) * xs + 63) / 64) * 64);
@@ -135,11 +142,21 @@ int check_problem(const kd_problem* p) {
     const int64_t ldt = (static_cast<int64_t>(p->chunk) * (p->dw_chunks > 1 ? p->dw_chunks : 1) + 7) / 8 * 8;
     if (256 * ldz * xs > 0x7FFFFFF0LL || 256 * ldt * xs > 0x7FFFFFF0LL) return KD_ERR_SHAPE;
   }
-  // One projection launch covers a chunk's (row tile, vocabulary tile) pairs
-  // with 512 work-items each; its work-item count must fit in 32 bits.
-  const int64_t ptiles = (static_cast<int64_t>(p->chunk) + kd::kProjBM - 1) / kd::kProjBM *
+  // One projection launch covers the (row tile, vocabulary tile) pairs of a
+  // chunk -- of a group of dw_chunks chunks in the backward -- with 512
+  // work-items each; its work-item count must fit in 32 bits, and so must
+  // that of the group's dH launch (row tiles x hidden tiles x V slices).
+  const int64_t grows = static_cast<int64_t>(p->chunk) * (p->dw_chunks > 1 ? p->dw_chunks : 1);
+  const int64_t ptiles = (grows + kd::kProjBM - 1) / kd::kProjBM *
                          ((static_cast<int64_t>(p->v) + kd::kProjBN - 1) / kd::kProjBN);
   if (ptiles > kMaxProjTiles) return KD_ERR_SHAPE;
+  {
+    int kslice = 0;
+    const int ldz = (p->v + kd::kProjBN - 1) / kd::kProjBN * kd::kProjBN;
+    const int split = kd::dh_split_for(p->chunk, p->d, ldz, &kslice);
+    const int64_t dtiles = (grows + kd::kDhBM - 1) / kd::kDhBM * ((p->d + kd::kDhBN - 1) / kd::kDhBN) * split;
+    if (dtiles > kMaxProjTiles) return KD_ERR_SHAPE;
+  }
   if (p->d % 8 != 0) return KD_ERR_ALIGN;
   return KD_OK;
 }
@@ -230,9 +247,11 @@ void launch_group_dw(ChunkArgs a, const kd_problem& p, const Layout& L, char* ba
   timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
 }
 
-// Arguments of one chunk's kernels.  `slot` is the chunk's place in its dW
-// group: its dZ goes to slot `slot` of the dZ region and its H^T to the
-// columns from slot * chunk (the chunks before it in the group are full).
+// Arguments of the kernels of `rows` rows from row0 (a chunk, a forward pass
+// or a backward group).  `slot` (single-call path, which walks the chunks of
+// a dW group one by one) is the chunk's place in its group: its dZ goes to
+// slot `slot` of the dZ region and its H^T to the columns from slot * chunk
+// (the chunks before it in the group are full).
 ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const void* H, const void* W,
                      const int32_t* ids, const void* logits, const uint8_t* mask, int64_t row0, int rows,
                      bool cached = false, int slot = 0) {
@@ -270,7 +289,7 @@ ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const voi
   a.ht = base + L.ht;
   a.ldt = L.ldt;
   a.hk = base + L.hk;
-  a.ldk = p.chunk;
+  a.ldk = L.rows;
   a.ht_off = slot * p.chunk;
   a.ht_span = rows;
   return a;
@@ -431,22 +450,25 @@ int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W, const i
   (void)hipGetLastError();
   const Layout L = layout_for(p);
   char* base = ws_base(workspace);
-  const int64_t nchunks = (p.n + p.chunk - 1) / p.chunk;
-  const int G = dw_group(p);
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const int64_t row0 = c * p.chunk;
-    const int rows = static_cast<int>(p.n - row0 < p.chunk ? p.n - row0 : p.chunk);
-    const int slot = static_cast<int>(c % G);
-    const bool group_end = slot == G - 1 || c == nchunks - 1;
-    ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows, false, slot);
-    if (group_end) a.ht_span = (a.ht_off + rows + 31) / 32 * 32 - a.ht_off;
+  // groups of dw_chunks chunks: each kernel runs once over a group's rows
+  // (per row the same arithmetic as chunk by chunk; dH keeps one chunk's
+  // split of the V reduction), and one dW GEMM reads the group's dZ
+  const int64_t unit = L.rows;
+  const int64_t ngroups = (p.n + unit - 1) / unit;
+  for (int64_t c = 0; c < ngroups; ++c) {
+    const int64_t row0 = c * unit;
+    const int rows = static_cast<int>(p.n - row0 < unit ? p.n - row0 : unit);
+    ChunkArgs a = chunk_args(p, L, base, H, W, t_ids, t_logits, mask, row0, rows);
+    a.ht_span = (rows + 31) / 32 * 32;  // H_c^T zero-padded to a whole k tile
     timed(KD_K_PREP, s, [&] { kd::launch_prep(a, s); });
     timed(KD_K_H_TILE, s, [&] { kd::launch_tile_h(a, s); });
     timed(KD_K_BWD_DZ, s, [&] { kd::launch_bwd_dz(a, lse + row0, grad_loss, s); });
+    // one dH launch per group: the chunks' launches one by one were slower
+    // (measured), as each then reads a dZ the cache no longer holds
     timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
     if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
     timed(KD_K_H_TRANSPOSE, s, [&] { kd::launch_transpose_h(a, s); });
-    if (group_end) launch_group_dw(a, p, L, base, dW, s);
+    timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
   }
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }

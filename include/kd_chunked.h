@@ -89,9 +89,12 @@ typedef struct kd_problem {
   int32_t x_dtype; /* kd_dtype of H and W (the projection's compute dtype)      */
   int32_t t_dtype; /* kd_dtype of the teacher logits                            */
   float tau;       /* temperature: 0 or 1 = the plain loss, else in [0.01, 100]  */
-  int32_t dw_chunks; /* chunks whose dZ one dW GEMM reads, 0..8 (0 = 1): the
-                        workspace then holds that many chunks of dZ, and dW is
-                        read and written once per group instead of per chunk */
+  int32_t dw_chunks; /* chunks the backward takes at once, 0..8 (0 = 1): it
+                        runs each of its kernels once per group of that many
+                        chunks (the workspace holds their dZ), so dW is read
+                        and written once per group instead of per chunk; the
+                        results do not change (dH is summed over the V slices
+                        of one chunk's split either way) */
 } kd_problem;
 
 /* Bytes of workspace the fwd and bwd calls need for `prob`.  Depends on

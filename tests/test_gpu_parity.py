@@ -56,6 +56,11 @@ SMALL = [
     (257, 200, 777, 256, 100, "bf16", "none"),
     (1024, 384, 5000, 100, 512, "f32", "random:100"),
     (600, 520, 2000, 64, 256, "bf16", "random:40"),
+    # hidden sizes where dW takes 256 x 320 tiles (they pad d less than 384 x 256 tiles):
+    # whole 320-wide tiles, and a partly filled last one
+    (450, 640, 3001, 50, 200, "f32", "random:30"),
+    (333, 960, 2500, 64, 333, "bf16", "none"),
+    (260, 1560, 1100, 40, 130, "f32", "tail:20"),
 ]
 
 
