@@ -6,16 +6,17 @@
 A step is one pass of the whole hot path over the workload: kd_chunked_fwd
 (per pass of up to 8 chunks: teacher renormalisation, fused projection +
 online logsumexp + top-K gather, merge, running-loss fold) then
-kd_chunked_bwd (per chunk: recomputed projection + closed-form dZ,
-dH = dZ W, dW += dZ^T H).  Inputs are
+kd_chunked_bwd (per group of --dw-chunks chunks, default 2: recomputed
+projection + closed-form dZ, dH = dZ W, dW += dZ^T H).  Inputs are
 seeded synthetic tensors already resident in HBM when timing starts; dW keeps
 accumulating across steps (it is zeroed once, outside the timed region).
 
 Prints ONE JSON line: tokens/s (value), TFLOP/s counted as 8*N*D*V per step
 and its fraction of the bf16 dense matrix-core peak, peak HBM GiB, a roofline
 record of the dominant kernel (per-kernel durations from HIP events recorded
-on the launch stream during the timed steps), and the fp64 CPU oracle timed
-on a bounded sample of the same workload.
+on the launch stream during a second pass of the same steps; the headline
+steps run without them), and the fp64 CPU oracle timed on a bounded sample of
+the same workload.
 """
 import argparse
 import json
@@ -48,6 +49,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt-oss-20b-32k")
     ap.add_argument("--chunk", type=int, default=None, help="override the workload's chunk size")
+    ap.add_argument("--dw-chunks", type=int, default=2,
+                    help="chunks the backward takes at once (kd_problem.dw_chunks): 2 keeps two chunks of dZ "
+                         "in the workspace and reads/writes dW once per two chunks")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="rows of the CPU oracle sample (about 15-20 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
@@ -128,9 +132,13 @@ def cpu_baseline(inp, rows_n):
     ids = inp["t_ids"][rows]
     lg = oracle.widen(inp["t_logits"][rows], wl.t_dtype)
     m = None if inp["mask"] is None else inp["mask"][rows]
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        cores = max([int(i.get("num_threads", 1)) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
@@ -138,7 +146,7 @@ def cpu_baseline(inp, rows_n):
     oracle.kd_backward(Hs, Wx, ids, lg, m, want_dw=True)
     dt = time.perf_counter() - t0
     del np
-    return {"value": rows.size / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": rows.size / dt, "unit": "tokens/s", "cores": cores, "blas": blas, "kind": "oracle",
             "sample": f"{rows.size} seeded positions of {wl.name} (fp64 numpy dense forward + backward "
                       f"incl. their dW contribution), {dt:.1f} s",
             # linear extrapolation (the oracle's cost is per position): not measured
@@ -191,7 +199,7 @@ def main():
     H, W = dev(inp["H"], wl.x_dtype), dev(inp["W"], wl.x_dtype)
     ids, lg = dev(inp["t_ids"]), dev(inp["t_logits"], wl.t_dtype)
     mask = dev(inp["mask"])
-    prob = L.make_problem(H, W, ids, lg, chunk)
+    prob = L.make_problem(H, W, ids, lg, chunk, 1.0, args.dw_chunks)
     ws = L.workspace_for(prob, H.device)
     loss = torch.empty(1, dtype=torch.float32, device="cuda")
     lse = torch.empty(wl.n, dtype=torch.float32, device="cuda")
@@ -209,7 +217,8 @@ def main():
     torch.cuda.synchronize()
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    B.kd_profile_enable(True)
+    # the headline steps run with the library's per-kernel event recording off
+    B.kd_profile_enable(False)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # one event after each step as well (recording an event does not synchronise):
     # per-step times for the median / min next to the mean over the timed region
@@ -227,10 +236,21 @@ def main():
     step_stats = {"median": round(per_step[len(per_step) // 2] if len(per_step) % 2 else
                                   0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2]), 4),
                   "min": round(per_step[0], 4), "max": round(per_step[-1], 4)}
-    kern = B.kd_profile_all()
-    B.kd_profile_enable(False)
     peak_gib = torch.cuda.max_memory_allocated() / 2 ** 30
     loss_v = float(loss.item())
+    # per-kernel durations: a second pass of the same steps with HIP events recorded around every
+    # launch on the launch stream (kd_profile.h)
+    print(f"[bench] per-kernel pass, {args.steps} steps", file=sys.stderr, flush=True)
+    B.kd_profile_enable(True)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for _ in range(args.steps):
+        step()
+    p1.record(stream)
+    torch.cuda.synchronize()
+    kern = B.kd_profile_all()
+    B.kd_profile_enable(False)
+    profiled_ms = p0.elapsed_time(p1) / args.steps
 
     N, D, V = wl.n, wl.d, wl.v
     flops_step = 8.0 * N * D * V
@@ -293,14 +313,14 @@ def main():
             "ms_per_step": round(tau_ms, 4), "tokens_per_s": round(N / (tau_ms * 1e-3), 1),
             "tflops": round(flops_step / (tau_ms * 1e-3) / 1e12, 2), "loss": float(loss.item())}}
 
-        # dW over groups of two chunks (kd_problem.dw_chunks = 2): the workspace keeps two chunks of
-        # dZ and dW is read and written once per two chunks; same flops and results as the headline
-        # (bit for bit when the chunk is a multiple of the k tile)
+        # the backward chunk by chunk (kd_problem.dw_chunks = 1): one chunk of dZ in the workspace,
+        # dW read and written once per chunk; same flops and results as the headline
+        other = 1 if args.dw_chunks != 1 else 2
         del ws
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
-        prob_g = L.make_problem(H, W, ids, lg, chunk, 1.0, 2)
+        prob_g = L.make_problem(H, W, ids, lg, chunk, 1.0, other)
         wsg = L.workspace_for(prob_g, H.device)
 
         def step_groups():
@@ -315,8 +335,8 @@ def main():
         v1.record(stream)
         torch.cuda.synchronize()
         g_ms = v0.elapsed_time(v1) / vsteps
-        variants["dw_chunks_2"] = {
-            "entry": "kd_chunked_fwd + kd_chunked_bwd, dw_chunks = 2", "steps": vsteps,
+        variants[f"dw_chunks_{other}"] = {
+            "entry": f"kd_chunked_fwd + kd_chunked_bwd, dw_chunks = {other}", "steps": vsteps,
             "ms_per_step": round(g_ms, 4), "tokens_per_s": round(N / (g_ms * 1e-3), 1),
             "tflops": round(flops_step / (g_ms * 1e-3) / 1e12, 2),
             "peak_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 3)}
@@ -403,10 +423,11 @@ def main():
         "dtype": wl.x_dtype,
         "data": "synthetic (seeded; shapes and value recipe of the workload)",
         "config": {"workload": wl.name, "n": N, "d": D, "v": V, "k": wl.k, "chunk": chunk,
-                   "mask": wl.mask, "ids": wl.ids, "parallelism": "none (1 GPU)"},
+                   "dw_chunks": args.dw_chunks, "mask": wl.mask, "ids": wl.ids, "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2),
         "pct_peak": round(100.0 * tflops / peak, 2),
         "peak_gib": round(peak_gib, 3),
+        "profiled_ms_per_step": round(profiled_ms, 4),
         "loss": loss_v,
         "roofline": roofline,
         "kernels": kernels,

@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kd {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -200,9 +202,10 @@ struct StageLoader {
     return make_rsrc(op.ptr + base, static_cast<uint64_t>(static_cast<long>(op.k_lim - k0) * op.ld - op.r0) * SZ);
   }
 
-  // Issue instructions [I0, I1) of the k tile starting at k0 into LDS `dst`.
+  // Issue instructions [I0, I1) of the k tile starting at k0 into the stage
+  // at LDS byte address `dst` (wave-uniform: the m0 values stay scalar).
   template <int I0, int I1>
-  __device__ __forceinline__ void issue(const Operand<T>& op, const u32x4& rs, int k0, char* dst,
+  __device__ __forceinline__ void issue(const Operand<T>& op, const u32x4& rs, int k0, uint32_t dst,
                                         int wave) const {
     // k tiled: the buffer resource starts at the tile's block, whose k
     // padding holds zeros
@@ -210,10 +213,10 @@ struct StageLoader {
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const uint32_t o = KC && !KT ? voff[i] + static_cast<uint32_t>(k0 * SZ) : voff[i];
-      lds_dma16(rs, kc_ok ? o : kOOB, lds_addr(dst + (wave * NI + i) * 1024));
+      lds_dma16(rs, kc_ok ? o : kOOB, dst + static_cast<uint32_t>((wave * NI + i) * 1024));
     }
   }
-  __device__ __forceinline__ void issue_all(const Operand<T>& op, int k0, char* dst, int wave) const {
+  __device__ __forceinline__ void issue_all(const Operand<T>& op, int k0, uint32_t dst, int wave) const {
     issue<0, NI>(op, rsrc(op, k0), k0, dst, wave);
   }
 };
@@ -348,12 +351,16 @@ struct Gemm {
     LB lb;
     la.init(a, wave, lane);
     lb.init(b, wave, lane);
+    // stage addresses as 32-bit LDS byte addresses (scalar arithmetic)
+    const uint32_t lds0 = lds_addr(lds);
+    auto issue_tile = [&](int t) {
+      const uint32_t dst = lds0 + static_cast<uint32_t>((t % NS) * STAGE);
+      la.issue_all(a, k_begin + t * BK, dst, wave);
+      lb.issue_all(b, k_begin + t * BK, dst + A_BYTES, wave);
+    };
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t) {
-      if (t < nk) {
-        la.issue_all(a, k_begin + t * BK, lds + t * STAGE, wave);
-        lb.issue_all(b, k_begin + t * BK, lds + t * STAGE + A_BYTES, wave);
-      }
+      if (t < nk) issue_tile(t);
     }
     init(acc);
     if constexpr (Init::kLoads)
@@ -365,15 +372,16 @@ struct Gemm {
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[i] = read_a(lds, 0, wm, i, lane);
     read_b(b0, lds, 0, wn, lane);
-    for (int kt = 0; kt < nk; ++kt) {
+    // One k tile.  LOAD: issue the loads of tile kt+NS-1; MORE: a tile kt+1
+    // follows (read its step-0 fragments); wait: own tiles left in flight
+    // when tile kt+1 is needed.  The loop below runs the tiles that issue a
+    // load with constants for all three, so its body has no branch; the last
+    // NS-1 tiles run after it.
+    auto tile = [&](int kt, auto load_t, auto more_t, int wait) {
+      constexpr bool LOAD = decltype(load_t)::value, MORE = decltype(more_t)::value;
       const char* cur = lds + (kt % NS) * STAGE;
       const char* nxt = lds + ((kt + 1) % NS) * STAGE;
-      const bool more = kt + 1 < nk;
-      if (kt + NS - 1 < nk) {
-        char* dst = lds + ((kt + NS - 1) % NS) * STAGE;
-        la.issue_all(a, k_begin + (kt + NS - 1) * BK, dst, wave);
-        lb.issue_all(b, k_begin + (kt + NS - 1) * BK, dst + A_BYTES, wave);
-      }
+      if constexpr (LOAD) issue_tile(kt + NS - 1);
       // The scheduling fences keep every fragment read where it is written:
       // left alone, the scheduler sinks reads next to their consumers and
       // exposes the LDS latency at every step.
@@ -391,9 +399,9 @@ struct Gemm {
       // first B fragments of tile kt+1 are read one MFMA row earlier.  No
       // fragment of tile kt is read from LDS in step 1 either way.
       if constexpr (EARLY_BARRIER) {
-        wait_tiles(min(NS - 2, nk - kt - 2));
+        wait_tiles(wait);
         lds_barrier();
-        if (more) read_b(b0, nxt, 0, wn, lane);
+        if constexpr (MORE) read_b(b0, nxt, 0, wn, lane);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -401,14 +409,18 @@ struct Gemm {
         mma_row(acc, i, af[i], b1);
         __builtin_amdgcn_sched_barrier(0);
         if (!EARLY_BARRIER && i == 0) {
-          wait_tiles(min(NS - 2, nk - kt - 2));  // tile kt+1 has landed (own loads)
-          lds_barrier();                          // tile kt+1 visible; stage of kt free
-          if (more) read_b(b0, nxt, 0, wn, lane);
+          wait_tiles(wait);  // tile kt+1 has landed (own loads)
+          lds_barrier();     // tile kt+1 visible; stage of kt free
+          if constexpr (MORE) read_b(b0, nxt, 0, wn, lane);
         }
-        if (more) af[i] = read_a(nxt, 0, wm, i, lane);
+        if constexpr (MORE) af[i] = read_a(nxt, 0, wm, i, lane);
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    };
+    int kt = 0;
+    for (; kt < nk - (NS - 1); ++kt) tile(kt, std::true_type{}, std::true_type{}, NS - 2);
+    for (; kt < nk - 1; ++kt) tile(kt, std::false_type{}, std::true_type{}, nk - kt - 2);
+    tile(kt, std::false_type{}, std::false_type{}, 0);
     __syncthreads();
   }
 };
