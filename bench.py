@@ -294,7 +294,7 @@ def main():
         v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         # temperature-scaled loss, tau = 2: the same kernels, 1/tau folded into their exponent
         # scales and tau into the dZ coefficients (8 N D V flops, as the headline)
-        prob_t = L.make_problem(H, W, ids, lg, chunk, 2.0)
+        prob_t = L.make_problem(H, W, ids, lg, chunk, 2.0, args.dw_chunks)
 
         def step_tau():
             B.kd_chunked_fwd(prob_t, H, W, ids, lg, mask, loss, lse, None, None, ws, stream=stream)
@@ -309,7 +309,7 @@ def main():
         torch.cuda.synchronize()
         tau_ms = v0.elapsed_time(v1) / vsteps
         variants = {"temperature_2": {
-            "entry": "kd_chunked_fwd + kd_chunked_bwd, tau = 2", "steps": vsteps,
+            "entry": f"kd_chunked_fwd + kd_chunked_bwd, tau = 2, dw_chunks = {args.dw_chunks}", "steps": vsteps,
             "ms_per_step": round(tau_ms, 4), "tokens_per_s": round(N / (tau_ms * 1e-3), 1),
             "tflops": round(flops_step / (tau_ms * 1e-3) / 1e12, 2), "loss": float(loss.item())}}
 

@@ -131,6 +131,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p)));
 }
 
+// f(integral_constant<int, I>) for I = I0 .. I1-1, unrolled at compile time.
+template <int I0, int I1, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < I1) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, I1>(f);
+  }
+}
+
 // One operand of a block tile.
 template <typename T>
 struct Operand {
@@ -256,7 +265,7 @@ struct FragReader {
 
 // A_KT / B_KT: that operand is k tiled (KT above; requires it to be KC).
 template <typename T, int BM_, int BN_, bool A_KC, bool B_KC, int WAVES_M = 2, int WAVES_N = 4, int NS_ = 4,
-          bool EARLY_BARRIER = false, bool A_KT = false, bool B_KT = false>
+          bool EARLY_BARRIER = false, bool A_KT = false, bool B_KT = false, bool SPREAD = false>
 struct Gemm {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int SZ = static_cast<int>(sizeof(T));
@@ -381,19 +390,36 @@ struct Gemm {
       constexpr bool LOAD = decltype(load_t)::value, MORE = decltype(more_t)::value;
       const char* cur = lds + (kt % NS) * STAGE;
       const char* nxt = lds + ((kt + 1) % NS) * STAGE;
-      if constexpr (LOAD) issue_tile(kt + NS - 1);
+      // SPREAD: the loads of tile kt+NS-1 go out in slices after each MFMA
+      // row of step 0 (instructions [i NI / FM, (i + 1) NI / FM) after row
+      // i, A's first) instead of all before the first row
+      const int tn = kt + NS - 1;
+      const uint32_t dst = lds0 + static_cast<uint32_t>((tn % NS) * STAGE);
+      u32x4 rsa, rsb;
+      if constexpr (LOAD && SPREAD) {
+        rsa = la.rsrc(a, k_begin + tn * BK);
+        rsb = lb.rsrc(b, k_begin + tn * BK);
+      }
+      if constexpr (LOAD && !SPREAD) issue_tile(tn);
       // The scheduling fences keep every fragment read where it is written:
       // left alone, the scheduler sinks reads next to their consumers and
       // exposes the LDS latency at every step.
       read_b(b1, cur, 1, wn, lane);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      static_for<0, FM>([&](auto I) {
+        constexpr int i = decltype(I)::value;
         mma_row(acc, i, af[i], b0);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (LOAD && SPREAD) {
+          constexpr int g0 = i * NI / FM, g1 = (i + 1) * NI / FM;
+          constexpr int a0 = g0 < LA::NI ? g0 : LA::NI, a1 = g1 < LA::NI ? g1 : LA::NI;
+          constexpr int b0i = g0 > LA::NI ? g0 - LA::NI : 0, b1i = g1 > LA::NI ? g1 - LA::NI : 0;
+          if constexpr (a1 > a0) la.template issue<a0, a1>(a, rsa, k_begin + tn * BK, dst, wave);
+          if constexpr (b1i > b0i) lb.template issue<b0i, b1i>(b, rsb, k_begin + tn * BK, dst + A_BYTES, wave);
+        }
         af[i] = read_a(cur, 1, wm, i, lane);
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
       // The wait and barrier for tile kt+1: after the first MFMA row of step
       // 1, or (EARLY_BARRIER) before it, where b0 is already free so the
       // first B fragments of tile kt+1 are read one MFMA row earlier.  No

@@ -26,9 +26,11 @@ namespace kd {
 template <typename T>
 using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true>;
 // The loss projections read H_c through its k-tiled copy (k_tile_h): every
-// 128-byte line of it a load touches is read whole.
+// 128-byte line of it a load touches is read whole.  Their tile loads go out
+// in slices between the MFMA rows (SPREAD: measured faster for these, slower
+// for dH and dW).
 template <typename T>
-using ProjGemmT = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true, true>;
+using ProjGemmT = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true, true, false, true>;
 template <typename T>
 using DhGemm = Gemm<T, kDhBM, kDhBN, true, false, 2, 4, 4, true>;
 // dW reads H_c^T k tiled as well (k_transpose_h writes it so).
