@@ -800,6 +800,43 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
 // the top K is.  Rows with fewer than K sampled maxima take threshold 0 (every
 // logit; then v < 24 K <= 6144 <= kTopkCap).
 // One workgroup per row; the row's maxima are staged in LDS when they fit.
+// Rows with at most 256 kTopkRegKeys maxima (v up to 294912): each thread
+// holds its share in registers, so the 32 passes read no memory.  0 pads the
+// shares (no trial threshold is 0, so padding is never counted).
+constexpr int kTopkRegKeys = 48;
+__global__ __launch_bounds__(256) void k_topk_threshold_reg(const uint32_t* __restrict__ lmax, int nmax, int K,
+                                                            uint32_t* __restrict__ thr, int* __restrict__ cnt) {
+  __shared__ int s_c[2][4];
+  const int row = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const uint32_t* r = lmax + static_cast<long>(row) * nmax;
+  uint32_t x[kTopkRegKeys];
+#pragma unroll
+  for (int i = 0; i < kTopkRegKeys; ++i) {
+    const int t = tid + 256 * i;
+    x[i] = t < nmax ? r[t] : 0u;
+  }
+  uint32_t res = 0;
+  if (nmax >= K) {
+    // MSB first: the largest res with #{maxima >= res} >= K
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t trial = res | (1u << b);
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < kTopkRegKeys; ++i) c += x[i] >= trial ? 1 : 0;
+      c = wave_sum(c);
+      if (lane == 0) s_c[b & 1][w] = c;
+      __syncthreads();
+      if (s_c[b & 1][0] + s_c[b & 1][1] + s_c[b & 1][2] + s_c[b & 1][3] >= K) res = trial;
+    }
+  }
+  if (tid == 0) {
+    thr[row] = res;
+    cnt[row] = 0;
+  }
+}
+
+// Any number of maxima: staged in LDS when they fit, else read from memory
+// in every pass.
 __global__ __launch_bounds__(256) void k_topk_threshold(const uint32_t* __restrict__ lmax, int nmax, int K,
                                                         uint32_t* __restrict__ thr, int* __restrict__ cnt) {
   constexpr int kLdsKeys = 16384;
@@ -1092,7 +1129,11 @@ void launch_topk_maxima(const ChunkArgs& a, uint32_t* lmax, hipStream_t s) {
 }
 
 void launch_topk_threshold(const ChunkArgs& a, const uint32_t* lmax, uint32_t* thr, int* cnt, hipStream_t s) {
-  k_topk_threshold<<<dim3(a.rows), dim3(256), 0, s>>>(lmax, a.nvt * kTopkLanes, a.k, thr, cnt);
+  const int nmax = a.nvt * kTopkLanes;
+  if (nmax <= 256 * kTopkRegKeys)
+    k_topk_threshold_reg<<<dim3(a.rows), dim3(256), 0, s>>>(lmax, nmax, a.k, thr, cnt);
+  else
+    k_topk_threshold<<<dim3(a.rows), dim3(256), 0, s>>>(lmax, nmax, a.k, thr, cnt);
 }
 
 void launch_topk_collect(const ChunkArgs& a, const uint32_t* thr, int* cnt, uint64_t* cand, hipStream_t s) {

@@ -74,3 +74,27 @@ def vocab_sample(t_ids, mask, v, count, seed=0):
     rest = np.setdiff1d(np.arange(v), a)
     b = rng.choice(rest, size=count - a.size, replace=False)
     return np.sort(np.concatenate([a, b])).astype(np.int64), a
+
+
+def oracle_forward_all(inp, tau=1.0, slice_rows=4096, block=256, tag=""):
+    """The oracle's forward (lse, row loss, gathered logits, loss) for every
+    row of a stored input dict, in slices of rows with a progress line each
+    (rows are independent, so the slices change nothing)."""
+    import math
+
+    import oracle
+
+    wl = inp["wl"]
+    n = inp["H"].shape[0]
+    Wx = oracle.widen(inp["W"], wl.x_dtype)
+    lse = np.empty(n)
+    rl = np.empty(n)
+    zg = np.empty((n, inp["t_ids"].shape[1]))
+    for r0 in range(0, n, slice_rows):
+        r1 = min(n, r0 + slice_rows)
+        m = None if inp["mask"] is None else inp["mask"][r0:r1]
+        f = oracle.kd_forward(oracle.widen(inp["H"][r0:r1], wl.x_dtype), Wx, inp["t_ids"][r0:r1],
+                              oracle.widen(inp["t_logits"][r0:r1], wl.t_dtype), m, block=block, tau=tau)
+        lse[r0:r1], rl[r0:r1], zg[r0:r1] = f["lse"], f["row_loss"], f["zg"]
+        log(f"[{tag}] oracle forward rows {r1}/{n}")
+    return {"lse": lse, "row_loss": rl, "zg": zg, "loss": math.fsum(rl.tolist())}

@@ -28,7 +28,7 @@ import oracle
 from chunked_kl_loss_row_amd import binding as B
 from chunked_kl_loss_row_amd import inputs
 from chunked_kl_loss_row_amd import loss as L
-from gpu_helpers import log, rel, rel_fro, upload, vocab_sample
+from gpu_helpers import log, oracle_forward_all, rel, rel_fro, upload, vocab_sample
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -93,11 +93,12 @@ def test_largest_vocabulary(xd, v):
     log(f"oracle on {rows.size} rows")
     _check_rows(f, dH, inp, xd, rows, g, tl, tdh, block=4)
     # dW rows over all positions: the last vocabulary tile and a seeded sample
-    # of the others (half teacher ids), from the GPU's lse (checked above)
+    # of the others (half teacher ids), from the oracle's own lse of every row
     voc = np.unique(np.concatenate([np.arange(v - 384, v),
                                     vocab_sample(inp["t_ids"], inp["mask"], v - 384, 256, seed=5)[0]]))
+    ref_all = oracle_forward_all(inp, block=4, tag="largest vocabulary")
     ref_u = oracle.dw_vocab_rows(inp["H"], inp["W"], xd, inp["t_ids"], oracle.widen(inp["t_logits"], wl.t_dtype),
-                                 inp["mask"], f["lse"].cpu().numpy(), voc, g=g)
+                                 inp["mask"], ref_all["lse"], voc, g=g)
     e_dw = rel_fro(dW[torch.from_numpy(voc).cuda()].cpu().numpy(), ref_u)
     col = dW.double().sum(dim=0).abs().max().item()
     log(f"dW on {voc.size} vocabulary rows: rel_fro={e_dw:.3g}; largest column sum {col:.3g}")
@@ -127,10 +128,12 @@ def test_largest_chunk():
     e_dh2 = rel_fro(dH[chunk:].cpu().numpy(), oracle.kd_backward(
         oracle.widen(inp["H"][chunk:], "bf16"), oracle.widen(inp["W"], "bf16"), inp["t_ids"][chunk:],
         oracle.widen(inp["t_logits"][chunk:], "bf16"), inp["mask"][chunk:], g=g, want_dw=False)["dH"])
-    # the whole dW (every vocabulary row) over all positions, from the GPU's lse
+    # the whole dW (every vocabulary row) over all positions, from the oracle's own lse of every row
+    ref_all = oracle_forward_all(inp, slice_rows=1 << 20, block=65536, tag="largest chunk")
+    assert rel(loss, ref_all["loss"]) <= 1e-3
     log("oracle dW over all rows")
     ref_w = oracle.dw_vocab_rows(inp["H"], inp["W"], "bf16", inp["t_ids"], oracle.widen(inp["t_logits"], "bf16"),
-                                 inp["mask"], f["lse"].cpu().numpy(), np.arange(v), g=g, block=65536)
+                                 inp["mask"], ref_all["lse"], np.arange(v), g=g, block=65536)
     e_dw = rel_fro(dW.cpu().numpy(), ref_w)
     log(f"second chunk rel_fro dH={e_dh2:.3g}; rel_fro dW={e_dw:.3g}")
     assert e_dh2 <= 1e-2 and e_dw <= 1e-2

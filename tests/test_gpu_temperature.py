@@ -15,7 +15,7 @@ import torch
 import oracle
 from chunked_kl_loss_row_amd import inputs
 from chunked_kl_loss_row_amd import loss as L
-from gpu_helpers import dev, log, rel, rel_fro, run_hip, upload, vocab_sample
+from gpu_helpers import dev, log, oracle_forward_all, rel, rel_fro, run_hip, upload, vocab_sample
 
 pytestmark = pytest.mark.gpu
 
@@ -109,11 +109,13 @@ def test_gather_bit_exact_tempered():
 @pytest.mark.timeout(900)
 def test_gpt_oss_full_size_tempered_sampled():
     """The 32K gpt-oss workload in full at tau = 2 in the bench's launch
-    configuration, checked on 512 seeded rows (lse, row loss, dH), on 256
-    vocabulary rows of the full run's dW (over all positions) and, with the
-    mask restricted to the sampled rows, the loss and the whole dW; plus the
-    size-independent properties (L >= 0, loss = sum of row losses, vanishing
-    vocabulary sums of dW)."""
+    configuration (dw_chunks = 2), checked against the oracle's forward over
+    every row (the loss, every row's lse and row loss), on 512 seeded rows
+    (dH), on 256 vocabulary rows of the full run's dW (over all positions,
+    formed by the oracle from its own lse) and, with the mask restricted to
+    the sampled rows, the loss and the whole dW; plus the size-independent
+    properties (L >= 0, loss = sum of row losses, vanishing vocabulary sums of
+    dW).  No oracle call receives a GPU output."""
     import math
     tau = 2.0
     wl = inputs.workload("gpt-oss-20b-32k")
@@ -122,9 +124,9 @@ def test_gpt_oss_full_size_tempered_sampled():
     d = upload(inp)
     log("case gpt-oss tempered: full forward + backward")
     f = L.forward(d["H"], d["W"], d["t_ids"], d["t_logits"], d["mask"], chunk=wl.chunk, row_loss=True,
-                  temperature=tau)
+                  temperature=tau, dw_chunks=2)
     dH, dW = L.backward(d["H"], d["W"], d["t_ids"], d["t_logits"], d["mask"], f["lse"], None, chunk=wl.chunk,
-                        workspace=f["workspace"], temperature=tau)
+                        workspace=f["workspace"], temperature=tau, dw_chunks=2)
     torch.cuda.synchronize()
     loss = float(f["loss"].item())
     rl_all = f["row_loss"].cpu().numpy()
@@ -137,11 +139,16 @@ def test_gpt_oss_full_size_tempered_sampled():
     dH_s = dH[rows_t].cpu().numpy()
     voc, hit = vocab_sample(inp["t_ids"], inp["mask"], wl.v, 256, seed=3)
     dW_u = dW[torch.from_numpy(voc).cuda()].cpu().numpy()
-    lse_all = f["lse"].cpu().numpy()
     del dH, dW
+    ref_all = oracle_forward_all(inp, tau=tau, tag="gpt-oss tempered")
+    log(f"case gpt-oss tempered: loss gpu={loss:.9g} oracle={ref_all['loss']:.9g}")
+    assert rel(loss, ref_all["loss"]) <= 1e-3
+    np.testing.assert_allclose(f["lse"].cpu().numpy(), ref_all["lse"], rtol=1e-5, atol=0)
+    assert np.all(np.abs(rl_all - ref_all["row_loss"]) <= 1e-3 * (1.0 + np.abs(ref_all["row_loss"])))
     log("case gpt-oss tempered: oracle dW on 256 vocab rows over all positions")
     ref_u = oracle.dw_vocab_rows(inp["H"], inp["W"], wl.x_dtype, inp["t_ids"],
-                                 oracle.widen(inp["t_logits"], wl.t_dtype), inp["mask"], lse_all, voc, tau=tau)
+                                 oracle.widen(inp["t_logits"], wl.t_dtype), inp["mask"], ref_all["lse"], voc,
+                                 tau=tau)
     is_hit = np.isin(voc, hit)
     e_hit, e_uni = rel_fro(dW_u[is_hit], ref_u[is_hit]), rel_fro(dW_u[~is_hit], ref_u[~is_hit])
     log(f"case gpt-oss tempered: full-run dW vocab rows rel_fro hit={e_hit:.3g} uniform={e_uni:.3g}")
@@ -163,9 +170,9 @@ def test_gpt_oss_full_size_tempered_sampled():
     sub &= inp["mask"]
     sub_t = torch.from_numpy(sub).cuda()
     f2 = L.forward(d["H"], d["W"], d["t_ids"], d["t_logits"], sub_t, chunk=wl.chunk, workspace=f["workspace"],
-                   temperature=tau)
+                   temperature=tau, dw_chunks=2)
     _, dW2 = L.backward(d["H"], d["W"], d["t_ids"], d["t_logits"], sub_t, f2["lse"], None, chunk=wl.chunk,
-                        workspace=f["workspace"], temperature=tau)
+                        workspace=f["workspace"], temperature=tau, dw_chunks=2)
     torch.cuda.synchronize()
     ref_loss2 = math.fsum(ref_f["row_loss"][sub[rows] != 0].tolist())
     assert rel(float(f2["loss"].item()), ref_loss2) <= 1e-3
