@@ -44,10 +44,12 @@
  *  - arguments are checked on the host before anything is enqueued; on any
  *    error the call returns a non-zero kd_status and enqueues nothing;
  *  - no exception crosses the ABI.
- * Preconditions that are NOT checked: on unmasked rows the ids lie in [0,v)
- * (ids outside it are never matched; memory stays safe but the result is
- * meaningless); the backward gets the same inputs as the forward that
- * produced `lse`.  Repeated ids within a row are handled term by term.
+ * Preconditions that are NOT checked: on unmasked rows the ids lie in [0,v);
+ * the backward gets the same inputs as the forward that produced `lse`.
+ * An id outside [0,v) (negative, or >= v) matches no vocabulary entry: its
+ * gathered logit reads as 0 and it adds no -p term to dZ, while its p still
+ * counts in sum_k p_ik and sum_k p_ik log p_ik (memory stays safe; the loss
+ * is no longer a KL).  Repeated ids within a row are handled term by term.
  * Non-finite inputs propagate to the outputs; no error is raised.
  */
 #ifndef KD_CHUNKED_H
@@ -208,7 +210,7 @@ int kd_chunked_fwd_noalloc(const kd_problem* prob, const void* H, const void* W,
  * The cache holds, per position, the K most probable teacher tokens
  * (agentlenshq.com page, section "1. Top-K Logit Cachingによるオフライン
  * 蒸留"): K distinct ids of the vocabulary.  The loss calls do not check
- * this; an id outside [0,v) is never matched, so the result is meaningless.
+ * this; an id outside [0,v) matches no vocabulary entry (see above).
  * This call counts, over unmasked rows only (mask NULL = every row):
  *   out[0]  rows with an id outside [0, prob->v)
  *   out[1]  rows with an id that occurs more than once in the row

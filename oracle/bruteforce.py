@@ -60,7 +60,7 @@ def loss(H, W, ids, logits, mask=None, tau=1):
             row = mpmath.mpf(0)
             for kk in range(len(a)):
                 p = mpmath.exp(a[kk]) / za
-                q = mpmath.exp(z[int(ids[i][kk])]) / partition
+                q = mpmath.exp(_z_at(z, ids[i][kk])) / partition
                 if p != 0:
                     row += p * mpmath.log(p / q)
             row *= t * t
@@ -118,7 +118,15 @@ def _loss_mp(Hm, Wm, ids, logits, mask, t):
         za = mpmath.fsum(mpmath.exp(x) for x in a)
         for kk in range(len(a)):
             p = mpmath.exp(a[kk]) / za
-            q = mpmath.exp(z[int(ids[i][kk])]) / partition
+            q = mpmath.exp(_z_at(z, ids[i][kk])) / partition
             if p != 0:
                 total += p * mpmath.log(p / q)
     return total * t * t
+
+
+def _z_at(z, idx):
+    """The (tempered) student logit of token ``idx``; an id outside the
+    vocabulary matches no entry and its logit is taken as 0 (the reading for
+    records that break the cache's contract)."""
+    j = int(idx)
+    return z[j] if 0 <= j < len(z) else mpmath.mpf(0)

@@ -27,6 +27,10 @@ vocabulary-by-position grid -- written out in fp64 with numpy:
 * loss: reading: forward KL(teacher || student) restricted to the K cached ids,
   summed over unmasked positions:
   ``L = sum_i m_i sum_k p_ik (log p_ik - z_{i,t_ik} + lse_i)``.
+  Reading for records that break the cache's contract (ids outside [0, V)):
+  such an id matches no vocabulary entry -- its gathered logit ``z_{i,t_ik}``
+  is taken as 0 and it adds no term to dZ, while its ``p_ik`` still counts in
+  ``sum_k p_ik`` and ``sum_k p_ik log p_ik``.
 * gradient: the pages mention, without printing it, a closed-form gradient
   behind the fused chunked loss (aihot.vn page, section "Mô hình học sinh thu
   được").  From the definition above,
@@ -143,7 +147,9 @@ def kd_forward(H: np.ndarray, W: np.ndarray, t_ids: np.ndarray, t_logits: np.nda
             continue
         li = np.nonzero(live)[0]
         ids = np.asarray(t_ids[sel[li]], dtype=np.int64)
-        zg_b = np.take_along_axis(z[li], ids, axis=1)
+        # an id outside [0, V) matches no vocabulary entry: its gathered logit is 0
+        inside = (ids >= 0) & (ids < z.shape[1])
+        zg_b = np.where(inside, np.take_along_axis(z[li], np.where(inside, ids, 0), axis=1), 0.0)
         p, negent, s = teacher_distribution(t_logits[sel[li]], tau)
         zg[b0 + li] = zg_b
         # tau^2 sum_k p (log p - (z_t / tau - lse)) = tau^2 (negent - sum_k p z_t / tau + s * lse)
@@ -184,9 +190,10 @@ def kd_backward(H: np.ndarray, W: np.ndarray, t_ids: np.ndarray, t_logits: np.nd
         lse_b = row_logsumexp(z)
         p, _, s = teacher_distribution(t_logits[sel[live]], tau)
         dz = s[:, None] * np.exp(z - lse_b[:, None])
+        ids_b = np.asarray(t_ids[sel[live]], dtype=np.int64).ravel()
+        inside = (ids_b >= 0) & (ids_b < V)  # an id outside [0, V) matches no column
         r_idx = np.repeat(np.arange(live.size), p.shape[1])
-        np.add.at(dz, (r_idx, np.asarray(t_ids[sel[live]], dtype=np.int64).ravel()),
-                  -p.ravel())
+        np.add.at(dz, (r_idx[inside], ids_b[inside]), -p.ravel()[inside])
         dz *= g * tau
         dH[b0 + live] = dz @ W
         if want_dw:

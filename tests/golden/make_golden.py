@@ -21,7 +21,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 import mpmath  # noqa: E402
 
 from oracle import bruteforce  # noqa: E402
-from oracle_cases import TINY, tiny_problem  # noqa: E402
+from oracle_cases import TINY, case_problem  # noqa: E402
 
 
 def s(x):
@@ -32,8 +32,9 @@ def main():
     out = {"source": "oracle/bruteforce.py at 50 digits; definition per the agentlenshq.com page, "
                      "sections '1. Top-K Logit Cachingによるオフライン蒸留' and '2. Fused Chunked KL Loss'",
            "cases": []}
-    for name, n, d, v, k, seed, masked in TINY:
-        H, W, ids, a, mask = tiny_problem(n, d, v, k, seed, masked)
+    for spec in TINY:
+        name, n, d, v, k, seed, masked = spec
+        H, W, ids, a, mask = case_problem(spec)
         L, lses, rls = bruteforce.loss(H.tolist(), W.tolist(), ids.tolist(), a.tolist(),
                                        None if mask is None else mask.tolist())
         dH, dW = bruteforce.grad_fd(H.tolist(), W.tolist(), ids.tolist(), a.tolist(),
@@ -58,8 +59,9 @@ def main():
     out = {"source": "oracle/bruteforce.py at 50 digits with a temperature tau: teacher softmax(a / tau), "
                      "student softmax(z / tau), tau^2 times the KL at the K ids",
            "cases": []}
-    for (name, n, d, v, k, seed, masked), tau in [(TINY[0], 2.5), (TINY[2], 0.6), (TINY[3], 1.7)]:
-        H, W, ids, a, mask = tiny_problem(n, d, v, k, seed, masked)
+    for spec, tau in [(TINY[0], 2.5), (TINY[2], 0.6), (TINY[3], 1.7)]:
+        name, n, d, v, k, seed, masked = spec
+        H, W, ids, a, mask = case_problem(spec)
         mk = None if mask is None else mask.tolist()
         L, lses, rls = bruteforce.loss(H.tolist(), W.tolist(), ids.tolist(), a.tolist(), mk, tau=tau)
         dH, dW = bruteforce.grad_fd(H.tolist(), W.tolist(), ids.tolist(), a.tolist(), mk, g=0.37, tau=tau)

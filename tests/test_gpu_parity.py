@@ -17,6 +17,7 @@ import torch
 
 import oracle
 from chunked_kl_loss_row_amd import inputs
+from chunked_kl_loss_row_amd import loss as L
 from gpu_helpers import dev, log, rel, rel_fro, run_hip, upload
 
 pytestmark = pytest.mark.gpu
@@ -249,3 +250,32 @@ def test_autograd_wrapper():
     assert rel(lo.item(), ref["loss"]) <= 1e-5
     assert rel_fro(h.grad.cpu().numpy(), ref["dH"]) <= 1e-5
     assert rel_fro(w.grad.cpu().numpy(), ref["dW"]) <= 1e-5
+
+
+@pytest.mark.parametrize("xd", ["bf16", "f32"])
+def test_ids_outside_the_vocabulary_match_nothing(xd):
+    """Ids outside [0, v) -- v, v + 1 (padding columns of the last 384-wide
+    tile), -1, 2^24 + 5 (id 5 in its low 24 bits) and INT_MIN (0 in its low
+    24 bits) -- match no vocabulary entry: gathered logit 0, no -p in dZ, p
+    still counted (the oracle's reading for such records).  Both entry points
+    against the oracle, and bit for bit with each other."""
+    n, d, v, k, chunk = 300, 64, 2001, 16, 128
+    wl = inputs.custom(n, d, v, k, chunk, x_dtype=xd, mask="random:20", tag=980)
+    inp = inputs.make_inputs(wl, seed=6)
+    bad = [v, v + 1, -1, (1 << 24) + 5, -(1 << 31)]
+    rows = np.arange(0, n, 7)
+    for j, r in enumerate(rows):
+        inp["t_ids"][r, j % k] = bad[j % len(bad)]
+    inp["mask"][rows] = 1
+    log(f"case unmatched ids {xd}: {rows.size} rows")
+    d_ = upload(inp)
+    out = run_hip(d_, chunk, g=0.37)
+    ref = oracle.run(inp, g=0.37)
+    tl, tg = (1e-5, 1e-5) if xd == "f32" else (1e-3, 1e-2)
+    _cmp(inp, out, ref, tl, tg, tag=f"unmatched-{xd}")
+    assert np.all(out["zg"][inp["t_ids"] < 0] == 0.0) and np.all(out["zg"][inp["t_ids"] >= v] == 0.0)
+    gl = torch.tensor([0.37], dtype=torch.float32, device="cuda")
+    one = L.forward_backward(d_["H"], d_["W"], d_["t_ids"], d_["t_logits"], d_["mask"], gl, chunk=chunk)
+    torch.cuda.synchronize()
+    assert float(one["loss"].item()) == out["loss"]
+    assert torch.equal(one["dH"], out["dH"]) and torch.equal(one["dW"], out["dW"])

@@ -34,11 +34,15 @@ MUTATIONS = [
      "(- (p * zg_b).sum(axis=1) / tau + s * lse_b[li])"),
     ("dropped lse term", "(negent - (p * zg_b).sum(axis=1) / tau + s * lse_b[li])",
      "(negent - (p * zg_b).sum(axis=1) / tau)"),
-    ("gather off by one", "zg_b = np.take_along_axis(z[li], ids, axis=1)",
-     "zg_b = np.take_along_axis(z[li], (ids + 1) % z.shape[1], axis=1)"),
+    ("gather off by one", "np.take_along_axis(z[li], np.where(inside, ids, 0), axis=1)",
+     "np.take_along_axis(z[li], np.where(inside, (ids + 1) % z.shape[1], 0), axis=1)"),
+    ("unmatched ids wrap in the gather", "inside = (ids >= 0) & (ids < z.shape[1])",
+     "inside = np.ones(ids.shape, dtype=bool); ids = ids % z.shape[1]"),
+    ("unmatched ids wrap in the scatter", "inside = (ids_b >= 0) & (ids_b < V)",
+     "inside = np.ones(ids_b.shape, dtype=bool); ids_b = ids_b % V"),
     ("mask inverted", "return (np.asarray(mask)[rows] != 0).astype(np.float64)",
      "return (np.asarray(mask)[rows] == 0).astype(np.float64)"),
-    ("scatter sign", "-p.ravel())", "p.ravel())"),
+    ("scatter sign", "-p.ravel()[inside])", "p.ravel()[inside])"),
     ("scatter dropped", "np.add.at(dz, (r_idx", "(lambda *a: None)(dz, (r_idx"),
     ("softmax not normalised", "dz = s[:, None] * np.exp(z - lse_b[:, None])",
      "dz = s[:, None] * np.exp(z)"),
@@ -109,7 +113,16 @@ def pins(mod):
         dW = np.array([[_f(x) for x in r] for r in c["dW"]])
         assert np.linalg.norm(b["dH"] - dH) <= 1e-10 * np.linalg.norm(dH)
         assert np.linalg.norm(b["dW"] - dW) <= 1e-10 * np.linalg.norm(dW)
-        np.testing.assert_allclose(b["dZ"].sum(axis=1), 0.0, atol=1e-13)
+        # each dZ row sums to zero when every id of the row matches a column
+        # (an unmatched id leaves its p out of the scatter: the row sums to it)
+        matched = np.all((ids >= 0) & (ids < W.shape[0]), axis=1)
+        np.testing.assert_allclose(b["dZ"].sum(axis=1)[matched], 0.0, atol=1e-13)
+        if not matched.all():
+            p = np.exp(a - a.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            live = np.ones(c["n"], bool) if mask is None else mask != 0
+            left = c["g"] * np.where((ids >= 0) & (ids < W.shape[0]), 0.0, p).sum(axis=1) * live
+            np.testing.assert_allclose(b["dZ"].sum(axis=1), left, atol=1e-13)
         sub = np.arange(W.shape[0])[::-2]
         dWs = mod.dw_vocab_rows(H, W, "f64", ids, a, mask, [_f(x) for x in c["lse"]], sub,
                                 g=c["g"], tau=tau, block=2)

@@ -21,7 +21,7 @@ import scipy.special as sps
 
 import oracle
 from oracle import bruteforce
-from oracle_cases import TINY, tiny_problem
+from oracle_cases import TINY, case_problem, tiny_problem
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -85,8 +85,7 @@ def test_golden_fixture_regenerates():
 
 @pytest.mark.parametrize("spec", TINY, ids=lambda s: s[0])
 def test_bruteforce_live(spec):
-    _, n, d, v, k, seed, masked = spec
-    H, W, ids, a, mask = tiny_problem(n, d, v, k, seed + 1000, masked, w_scale=2.5, logit_scale=5.0)
+    H, W, ids, a, mask = case_problem(spec, seed_offset=1000, w_scale=2.5, logit_scale=5.0)
     L, lses, rls = bruteforce.loss(H.tolist(), W.tolist(), ids.tolist(), a.tolist(),
                                    None if mask is None else mask.tolist())
     f = oracle.kd_forward(H, W, ids, a, mask)
