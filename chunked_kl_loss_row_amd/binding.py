@@ -12,7 +12,9 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkdchunk.so")
+# KDCHUNK_LIB names another build of the same library (e.g. the host
+# sanitizer build the ABI tests run under); default: the in-tree build
+LIB_PATH = os.environ.get("KDCHUNK_LIB") or os.path.join(_HERE, "libkdchunk.so")
 
 KD_OK, KD_ERR_NULL, KD_ERR_SHAPE, KD_ERR_DTYPE, KD_ERR_ALIGN, KD_ERR_WORKSPACE, KD_ERR_DEVICE, \
     KD_ERR_LAUNCH = range(8)
