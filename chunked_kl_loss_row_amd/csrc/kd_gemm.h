@@ -264,14 +264,19 @@ struct FragReader {
 };
 
 // A_KT / B_KT: that operand is k tiled (KT above; requires it to be KC).
+// TRANS: the matrix cores take B as their first operand, so atom (i, j)
+// holds the transposed product: element e of a lane is (row 32 i + (lane &
+// 31), column 32 j + 8 (e >> 2) + 4 (lane >> 5) + (e & 3)) of the wave tile,
+// i.e. each lane holds whole groups of 4 consecutive columns of FM rows.
 template <typename T, int BM_, int BN_, bool A_KC, bool B_KC, int WAVES_M = 2, int WAVES_N = 4, int NS_ = 4,
-          bool EARLY_BARRIER = false, bool A_KT = false, bool B_KT = false, bool SPREAD = false>
+          bool EARLY_BARRIER = false, bool A_KT = false, bool B_KT = false, bool SPREAD = false, bool TRANS = false>
 struct Gemm {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int SZ = static_cast<int>(sizeof(T));
   static constexpr int BK = 64 / SZ;             // k per tile
   static constexpr int NS = NS_;                 // LDS stages
   static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int WAVES_ROWS = WAVES_M, WAVES_COLS = WAVES_N;
   static constexpr int NT = 64 * NWAVES;         // two waves per SIMD by default
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
@@ -295,7 +300,12 @@ struct Gemm {
   }
   __device__ __forceinline__ static void mma_row(f32x16 (&acc)[FM][FN], int i, const u32x4& a, const u32x4 (&b)[FN]) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) Elem<T>::mma(acc[i][j], a, b[j]);
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (TRANS)
+        Elem<T>::mma(acc[i][j], b[j], a);
+      else
+        Elem<T>::mma(acc[i][j], a, b[j]);
+    }
   }
   // wait until at most `tiles` tiles of this wave's loads are in flight
   __device__ __forceinline__ static void wait_tiles(int tiles) {

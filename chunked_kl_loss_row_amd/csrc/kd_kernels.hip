@@ -31,6 +31,10 @@ using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true>;
 // for dH and dW).
 template <typename T>
 using ProjGemmT = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true, true, false, true>;
+// The forward projection takes its tile transposed in the accumulators
+// (TRANS): its epilogue then works on whole row segments held in registers.
+template <typename T>
+using ProjGemmX = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true, true, false, true, true>;
 template <typename T>
 using DhGemm = Gemm<T, kDhBM, kDhBN, true, false, 2, 4, 4, true>;
 // dW reads H_c^T k tiled as well (k_transpose_h writes it so).
@@ -210,12 +214,15 @@ __device__ __forceinline__ void proj_tile(int t, int rtn, int nvt, int& vt, int&
 // ---------------------------------------------------------------------------
 // forward: projection + per-tile online (max, sum exp) + top-K gather
 // ---------------------------------------------------------------------------
-// Tile (rt, vt): z = H[rt rows] W[vt vocab]^T on matrix cores.  The epilogue
-// stages z (fp32) in LDS, reduces each row to the tile's max and sum of
-// exp(z - max) and copies z at the row's teacher ids that fall in the tile
-// (the gather is a copy of the accumulator, bit for bit).  Logits reach HBM
-// only in the single-call path (zc != null), which keeps the chunk's fp32
-// logits in the workspace for the dZ pass.
+// Tile (rt, vt): z = H[rt rows] W[vt vocab]^T on matrix cores, transposed in
+// the accumulators (each lane holds 4 rows x 48 columns of its wave tile, in
+// groups of 4 consecutive columns).  The epilogue works on the registers:
+// each wave reduces its 96 columns of a row to (max m_w, sum of exp((z -
+// m_w) / tau)), the two lanes sharing a row combine theirs, and one thread per
+// row folds the four waves' pairs into the tile's (max, sum).  The lane
+// holding a teacher id's column copies z there (a copy of the accumulator,
+// bit for bit).  Logits reach HBM only in the single-call path (zc != null),
+// which keeps the chunk's fp32 logits in the workspace for the dZ pass.
 template <typename T>
 __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ hk, int ldk, const T* __restrict__ W,
                                                      int rows, int d, int v, int nvt, int K,
@@ -224,10 +231,12 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ hk, i
                                                      float* __restrict__ zgs, float* __restrict__ pm,
                                                      float* __restrict__ ps, float* __restrict__ zc,
                                                      int ldz, float t2) {
-  using G = ProjGemmT<T>;
-  __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
+  using G = ProjGemmX<T>;
+  static_assert(G::WAVES_COLS == 4 && G::FN * 32 == G::WN, "the fold below takes four waves per row");
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
   __shared__ uint32_t s_hit[G::BM][kMaxHits];  // (column in tile << 8) | key slot
+  __shared__ float2 s_part[G::WAVES_COLS][G::BM];  // per wave: (max, sum) of its columns
   const int rtn = (rows + G::BM - 1) / G::BM;
   const int t = xcd_tile(blockIdx.x, rtn * nvt);
   if (t < 0) return;
@@ -250,66 +259,99 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ hk, i
   f32x16 acc[G::FM][G::FN];
   const Operand<T> A{hk, ldk, static_cast<long>((d + G::BK - 1) / G::BK) * ldk * G::BK, rt * G::BM, rows, d};
   const Operand<T> B{W, d, static_cast<long>(v) * d, vt * G::BN, v, d};
-  G::run(A, B, 0, d, smem, acc);
+  G::run(A, B, 0, d, smem, acc);  // ends with a barrier: the tables above are visible
 
-  // The epilogue's barriers order LDS only: the global writes of one stage
-  // pass stay in flight through the next.
-  float* stage = reinterpret_cast<float*>(smem);
-  const int ncols = min(G::BN, v - vt * G::BN);
-  const int g16 = tid >> 4, l16 = tid & 15;
+  const int lane = tid & 63, wave = tid >> 6, wm = wave / G::WAVES_COLS, wn = wave % G::WAVES_COLS;
+  const int half = lane >> 5;
+  // column in tile of element e of atom j: c0 + 32 j + 8 (e >> 2) + (e & 3)
+  const int c0 = wn * G::WN + 4 * half;
+  const int r0 = wm * G::WM + (lane & 31);  // row in tile of atom row i: r0 + 32 i
+  if (zc) {  // single-call path: keep the fp32 logits of the chunk
 #pragma unroll
-  for (int h = 0; h < G::BM / kStageRows; ++h) {
-    stage_slice<G>(stage, acc, h);
-    lds_barrier();
-    for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
-      const int row = h * kStageRows + rr, grow = rt * G::BM + row;
-      if (grow >= rows) break;
-      f32x4 x[G::BN / 64];
+    for (int i = 0; i < G::FM; ++i) {
+      const int grow = rt * G::BM + r0 + 32 * i;
+      if (grow >= rows) continue;
+      float* zrow = zc + static_cast<long>(grow) * ldz + vt * G::BN + c0;
 #pragma unroll
-      for (int j = 0; j < G::BN / 64; ++j) x[j] = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + j * 64 + l16 * 4);
-      if (zc) {  // single-call path: keep the fp32 logits of the chunk
-        float* zrow = zc + static_cast<long>(grow) * ldz + vt * G::BN + l16 * 4;
+      for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-        for (int j = 0; j < G::BN / 64; ++j) *reinterpret_cast<f32x4*>(zrow + j * 64) = x[j];
-      }
-      if (ncols < G::BN) {  // columns past v take no part (exp2(-inf) = 0)
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(zrow + 32 * j + 8 * g) =
+              f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    }
+  }
+  // Teacher ids: the lane holding (row, column) copies the accumulator.
 #pragma unroll
-        for (int j = 0; j < G::BN / 64; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (j * 64 + l16 * 4 + e >= ncols) x[j][e] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < G::BN / 64; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, x[j][e]);
-      mx = group16_max(mx);
-      float sm = 0.f;
-      const float mx2 = mx * t2;  // t2 = log2(e) / tau: exp((z - mx) / tau) = 2^(z t2 - mx t2)
-#pragma unroll
-      for (int j = 0; j < G::BN / 64; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm += fast_exp2(fmaf(x[j][e], t2, -mx2));
-      sm = group16_sum(sm);
-      if (l16 == 0) {
-        pm[static_cast<long>(grow) * nvt + vt] = mx;
-        ps[static_cast<long>(grow) * nvt + vt] = sm;
-      }
-      const int lo = s_lo[row], hi = s_hi[row];
-      if (hi - lo <= kMaxHits) {
-        if (l16 < hi - lo) {
-          const uint32_t u = s_hit[row][l16];
-          zgs[static_cast<long>(grow) * K + (u & 0xFFu)] = stage[rr * kStagePitch + (u >> 8)];
-        }
+  for (int i = 0; i < G::FM; ++i) {
+    const int row = r0 + 32 * i, grow = rt * G::BM + row;
+    const int lo = s_lo[row], n = s_hi[row] - lo;
+    for (int q = 0; q < n; ++q) {
+      int col, slot;
+      if (n <= kMaxHits) {
+        const uint32_t u = s_hit[row][q];
+        col = static_cast<int>(u >> 8);
+        slot = static_cast<int>(u & 0xFFu);
       } else {
-        for (int j = lo + l16; j < hi; j += 16) {
-          const int col = static_cast<int>(keys[static_cast<long>(grow) * K + j] >> 8) - vt * G::BN;
-          zgs[static_cast<long>(grow) * K + j] = stage[rr * kStagePitch + col];
-        }
+        slot = lo + q;
+        col = static_cast<int>(keys[static_cast<long>(grow) * K + slot] >> 8) - vt * G::BN;
+      }
+      const int cw = col - wn * G::WN;
+      if (cw >= 0 && cw < G::WN && ((cw >> 2) & 1) == half) {
+        const int jc = cw >> 5, ec = (cw & 3) + 4 * ((cw >> 3) & 3);
+        float z = 0.f;
+#pragma unroll
+        for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) z = (j == jc && e == ec) ? acc[i][j][e] : z;
+        zgs[static_cast<long>(grow) * K + slot] = z;
       }
     }
-    lds_barrier();
+  }
+  const int ncols = min(G::BN, v - vt * G::BN);
+  if (ncols < G::BN) {  // columns past v take no part (exp2(-inf) = 0)
+#pragma unroll
+    for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (c0 + 32 * j + 8 * (e >> 2) + (e & 3) >= ncols) acc[i][j][e] = -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[i][j][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // t2 = log2(e) / tau: exp((z - mx) / tau) = 2^(z t2 - mx t2); a wave with
+    // no column left (mx = -inf) sums exp2(-inf) = 0
+    const float mx2 = mx == -INFINITY ? 0.f : mx * t2;
+    float sm = 0.f;
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sm += fast_exp2(fmaf(acc[i][j][e], t2, -mx2));
+    sm += __shfl_xor(sm, 32, 64);
+    if (half == 0) s_part[wn][r0 + 32 * i] = make_float2(mx, sm);
+  }
+  __syncthreads();
+  for (int r = tid; r < G::BM; r += G::NT) {
+    const int grow = rt * G::BM + r;
+    if (grow >= rows) break;
+    float2 p[G::WAVES_COLS];
+#pragma unroll
+    for (int w = 0; w < G::WAVES_COLS; ++w) p[w] = s_part[w][r];
+    float mx = p[0].x;
+#pragma unroll
+    for (int w = 1; w < G::WAVES_COLS; ++w) mx = fmaxf(mx, p[w].x);
+    const float mx2 = mx * t2;  // some wave holds a column below v: mx is finite
+    float sm = 0.f;
+#pragma unroll
+    for (int w = 0; w < G::WAVES_COLS; ++w) sm += p[w].y * fast_exp2(fmaf(p[w].x, t2, -mx2));
+    pm[static_cast<long>(grow) * nvt + vt] = mx;
+    ps[static_cast<long>(grow) * nvt + vt] = sm;
   }
 }
 
