@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "kd_chunked.h"
+#include "kd_gemm.h"  // blocked dZ layout (blk_pitch)
 #include "kd_internal.h"
 #include "kd_profile.h"
 #include "kd_topk.h"
@@ -83,10 +84,12 @@ Layout layout_for(const kd_problem& p, Mode mode = Mode::kLoss) {
   L.rl = take(C * 8);
   L.loss_acc = take(8);
   const bool loss = mode != Mode::kTopk;
-  L.dz = take(bwd ? C * static_cast<size_t>(L.ldz) * xs : 0);
+  // dZ and the cached logits are blocked (32 x 32 blocks): whole blocks of rows
+  L.dz = take(bwd ? (C + 31) / 32 * static_cast<size_t>(xs == 2 ? kd::blk_pitch<2>(L.ldz) : kd::blk_pitch<4>(L.ldz))
+                  : 0);
   L.dhp = take(bwd && L.split > 1 ? static_cast<size_t>(L.split) * C * static_cast<size_t>(p.d) * 4 : 0);
   // the single-call path keeps one chunk of fp32 logits at a time
-  L.zc = take(mode == Mode::kLossCached ? static_cast<size_t>(p.chunk) * static_cast<size_t>(L.ldz) * 4 : 0);
+  L.zc = take(mode == Mode::kLossCached ? (static_cast<size_t>(p.chunk) + 31) / 32 * kd::blk_pitch<4>(L.ldz) : 0);
   L.ldt = static_cast<int>((C + 31) / 32 * 32);  // whole k tiles of H_c^T
   L.ht = take(bwd ? static_cast<size_t>(L.ldt) * static_cast<size_t>(p.d) * xs : 0);
   // H_c in k tiles of 64 bytes (the A operand of every projection)
@@ -129,9 +132,10 @@ int check_problem(const kd_problem* p) {
   // temperature: 0 means 1; otherwise a finite value in [0.01, 100]
   if (!(p->tau == 0.f || (p->tau >= 0.01f && p->tau <= 100.f))) return KD_ERR_SHAPE;
   if (p->dw_chunks < 0 || p->dw_chunks > 8) return KD_ERR_SHAPE;
-  // The matrix-core tiles address a k-contiguous operand panel (256 rows of
-  // its leading dimension) with 32-bit byte offsets: dZ (leading dimension
-  // 384 * ceil(v / 384)) in dH must stay below 2^31 bytes per panel.  The
+  // The matrix-core tiles address an operand panel (256 rows of its leading
+  // dimension) with 32-bit byte offsets: dZ (leading dimension 384 * ceil(v
+  // / 384), blocked, every 32 rows one contiguous block row) in dH must stay
+  // below 2^31 bytes per panel.  The
   // rows of one dW group (dw_chunks * chunk, rounded up to 8) are held to the
   // same bound: the launch code and the kernels count group rows and the
   // transposed H_c's row offsets in 32-bit ints, and this cap keeps them, with
@@ -140,7 +144,7 @@ int check_problem(const kd_problem* p) {
     const int64_t xs = p->x_dtype == KD_BF16 ? 2 : 4;
     const int64_t ldz = (static_cast<int64_t>(p->v) + kd::kProjBN - 1) / kd::kProjBN * kd::kProjBN;
     const int64_t ldt = (static_cast<int64_t>(p->chunk) * (p->dw_chunks > 1 ? p->dw_chunks : 1) + 7) / 8 * 8;
-    if (256 * ldz * xs > 0x7FFFFFF0LL || 256 * ldt * xs > 0x7FFFFFF0LL) return KD_ERR_SHAPE;
+    if (256 * ldz * xs + 8 * kd::kBlPad > 0x7FFFFFF0LL || 256 * ldt * xs > 0x7FFFFFF0LL) return KD_ERR_SHAPE;
   }
   // One projection launch covers the (row tile, vocabulary tile) pairs of a
   // chunk -- of a group of dw_chunks chunks in the backward -- with 512
@@ -238,12 +242,18 @@ void timed(int kind, hipStream_t s, F&& launch) {
   if (a && b) g_prof_pending.push_back({kind, a, b});
 }
 
-// The dW GEMM of a group ends at chunk `a` (its last): one GEMM over the dZ
-// rows of all the group's chunks (their slots are contiguous) and the H^T
-// columns they wrote.
-void launch_group_dw(ChunkArgs a, const kd_problem& p, const Layout& L, char* base, float* dW, hipStream_t s) {
-  a.rows = a.ht_off + a.rows;  // rows of the whole group
-  a.dz = base + L.dz;
+// The dH and dW GEMMs of a group that ends at chunk `a` (its last), in the
+// single-call path: one GEMM each over the dZ rows of all the group's chunks
+// (their slots are contiguous), as in the two-call backward, and the H^T
+// columns they wrote.  dH keeps one chunk's split of the V reduction, so
+// every row's dH is the same as chunk by chunk.
+void launch_group_dh_dw(ChunkArgs a, const kd_problem& p, float* dH, float* dW, hipStream_t s) {
+  const int64_t group_row0 = a.ht_off;  // rows of the group before chunk `a`
+  a.rows = a.ht_off + a.rows;           // rows of the whole group
+  a.dz_row0 = 0;
+  float* dh = dH - group_row0 * p.d;    // dH of the group's first row (dH points at chunk `a`'s)
+  timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dh, s); });
+  if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dh, s); });
   timed(KD_K_BWD_DW, s, [&] { kd::launch_bwd_dw(a, dW, s); });
 }
 
@@ -281,7 +291,8 @@ ChunkArgs chunk_args(const kd_problem& p, const Layout& L, char* base, const voi
   a.ps = reinterpret_cast<float*>(base + L.ps);
   a.rl = reinterpret_cast<double*>(base + L.rl);
   a.loss_acc = reinterpret_cast<double*>(base + L.loss_acc);
-  a.dz = base + L.dz + static_cast<size_t>(slot) * p.chunk * static_cast<size_t>(L.ldz) * xs;
+  a.dz = base + L.dz;
+  a.dz_row0 = slot * p.chunk;
   a.dhp = reinterpret_cast<float*>(base + L.dhp);
   a.dh_split = L.split;
   a.dh_kslice = L.kslice;
@@ -514,10 +525,8 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, con
     timed(KD_K_MERGE, s, [&] { kd::launch_merge(a, lse + row0, nullptr, nullptr, s); });
     timed(KD_K_LOSS, s, [&] { kd::launch_loss_fold(a, p.chunk, c == 0, c == nchunks - 1, loss, s); });
     timed(KD_K_DZ_CACHED, s, [&] { kd::launch_dz_cached(a, lse + row0, grad_loss, s); });
-    timed(KD_K_BWD_DH, s, [&] { kd::launch_bwd_dh(a, dH + row0 * p.d, s); });
-    if (a.dh_split > 1) timed(KD_K_DH_REDUCE, s, [&] { kd::launch_dh_reduce(a, dH + row0 * p.d, s); });
     timed(KD_K_H_TRANSPOSE, s, [&] { kd::launch_transpose_h(a, s); });
-    if (group_end) launch_group_dw(a, p, L, base, dW, s);
+    if (group_end) launch_group_dh_dw(a, p, dH + row0 * p.d, dW, s);
   }
   return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_LAUNCH;
 }

@@ -7,6 +7,12 @@
 //   KT  -- k tiled (a KC operand re-laid out by k tile): element (r, k) at
 //          ptr[(k / BK) * ld * BK + r * BK + k % BK], ld = rows per k-tile
 //          block, zero-padded in k up to a whole tile.
+//   BL  -- blocked (dZ, as the dZ passes write it): a row-major [rows][ld]
+//          matrix whose 32 x 32 blocks are each stored as 16-byte granules of
+//          consecutive columns, granule-major: element (r, c) at byte
+//          blk_offset(r, c) below.  Read as KC (dH: r = chunk row, k = c) or
+//          as KO (dW: r = c, k = chunk row); either way a stage's loads are
+//          runs of 256 or 512 contiguous bytes.
 // The four contractions of the loss use: projection (KT, KC), dH = dZ W
 // (KC, KO), dW = dZ^T H (KO, KT); the teacher top-K passes (KC, KC).  A KC tile reads 64 bytes of each of its
 // rows, half of each 128-byte line it touches (the other half is the next k
@@ -22,6 +28,11 @@
 //   KC: [R rows][64 B of k], 16-byte chunk c of row r stored at c ^ ((r>>2)&3);
 //   KO: [BK rows of k][R entries], 16-byte chunk c of row k stored at
 //       c ^ fko(k) (bf16: 4*(k&3); fp32: 8*((k>>2)&1)).
+//   BL read as KO: [R / 32 blocks][granule g][BK rows of k][16 B], the k row
+//       of granule g stored at k ^ bl_swz(g) (the order of the global
+//       blocks, each run of granules loaded as one contiguous piece);
+//   BL read as KC: [4 chunks of the k tile][R rows][16 B] (the global order
+//       of the granules: lane after lane, 16-byte rows of one granule).
 // The swizzles make the matrix-core fragment reads bank-conflict free:
 //   KC: ds_read_b128, lane l -> row l%32, k chunk from l/32;
 //   KO bf16: ds_read_b64_tr_b16 (LDS transpose read), two per fragment;
@@ -62,6 +73,27 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 constexpr uint32_t kOOB = 0x80000000u;  // offset past every record count we set
+
+// Blocked layout: byte offset of element (r, c) of a [rows][ld] matrix of
+// SZ-byte elements (ld a multiple of 32; rows padded to a multiple of 32).
+// Each block row of 32 rows is followed by kBlPad bytes, so that block rows
+// do not start at the same offset modulo the memory channel interleave (at
+// ld = 201216, 32 rows of bf16 are an exact multiple of 4 KiB).
+constexpr long kBlPad = 256;
+template <int SZ>
+__host__ __device__ __forceinline__ long blk_pitch(long ld) { return 32 * ld * SZ + kBlPad; }
+template <int SZ>
+__host__ __device__ __forceinline__ long blk_offset(long r, long c, long ld) {
+  constexpr int VPG = 16 / SZ;  // elements per granule
+  return (r >> 5) * blk_pitch<SZ>(ld) + (c >> 5) * (1024 * SZ) + ((c & 31) / VPG) * 512 + (r & 31) * 16 +
+         (c % VPG) * SZ;
+}
+// k-row swizzle of granule g in a blocked stage read as KO (bf16: bits 2-3
+// of the 32 k rows; fp32: bits 0, 1 and 3 of the 16).
+template <int SZ>
+__device__ __forceinline__ int bl_swz(int g) {
+  return SZ == 2 ? (4 * (g & 1) | 8 * (g >> 1)) : ((g & 3) | ((g & 4) << 1));
+}
 
 // s_waitcnt immediate that waits for at most n outstanding vector-memory
 // operations and does not wait on the other counters (gfx9 encoding).
@@ -153,16 +185,20 @@ struct Operand {
 
 // Loads of one operand stage, R tile rows, NWAVES waves.  KT (with KC): the
 // operand is k tiled; the stage layout in LDS is the KC one.
-template <typename T, int R, bool KC, int NWAVES, bool KT = false>
+template <typename T, int R, bool KC, int NWAVES, bool KT = false, bool BL = false>
 struct StageLoader {
   static constexpr int VEC = Elem<T>::VEC;
   static constexpr int SZ = static_cast<int>(sizeof(T));
   static constexpr int BK = 64 / SZ;
+  static constexpr int GPB = 32 * SZ / 16;     // BL: granules per 32 columns of a block row
+  static constexpr int BLK = 32 * 32 * SZ;     // BL: bytes per 32 x 32 block
   static constexpr int NI = R * 64 / 1024 / NWAVES;  // 1 KiB wave instructions per wave per stage
   static constexpr int CPR = R * SZ / 16;     // KO: 16-byte chunks per k row
   static_assert(R * 64 % (1024 * NWAVES) == 0, "stage must split evenly over the waves");
   static_assert(KC || (CPR % 16 == 0), "k-outer tiles need >= 256 bytes per k row");
   static_assert(KC || !KT, "a k-tiled operand is k-contiguous within its tile");
+  static_assert(!(KT && BL), "one layout per operand");
+  static_assert(!BL || R % 32 == 0, "blocked tiles span whole blocks");
 
   // byte offset from the tile's base (k part excluded for KC); kOOB when the
   // row (KC) / column chunk (KO) lies outside the operand.  kOOB plus any k
@@ -181,7 +217,16 @@ struct StageLoader {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int S = (wave * NI + i) * 64 + lane;
-      if (KC) {
+      if (BL && KC) {  // LDS slot (chunk c, row r) <- granule c of row r (the k part is added per tile)
+        const int c = S / R, r = S % R;
+        voff[i] = op.r0 + r < op.r_lim ? static_cast<uint32_t>((r >> 5) * blk_pitch<SZ>(op.ld) + c * 512 + (r & 31) * 16)
+                                       : kOOB;
+      } else if (BL) {  // LDS slot (block cb, granule g, k row kq) <- k row kq ^ bl_swz(g)
+        const int kq = S % BK, g = (S / BK) % GPB, cb = S / (BK * GPB);
+        voff[i] = op.r0 + cb * 32 + g * VEC < op.r_lim
+                      ? static_cast<uint32_t>(cb * BLK + g * 512 + (kq ^ bl_swz<SZ>(g)) * 16)
+                      : kOOB;
+      } else if (KC) {
         const int r = S >> 2, p = S & 3;
         const int c = p ^ ((r >> 2) & 3);
         const long row_bytes = KT ? 64 : op.ld * SZ;
@@ -197,6 +242,14 @@ struct StageLoader {
   // Buffer resource of the k tile starting at k0 (wave-uniform).  For a
   // k-outer tile the record stops at row k_lim, so rows past it read as zero.
   __device__ __forceinline__ u32x4 rsrc(const Operand<T>& op, int k0) const {
+    if (BL) {  // extent counts the region's bytes / SZ
+      const char* p = reinterpret_cast<const char*>(op.ptr);
+      // KC: the tile's first block row; KO: the block row of k tile k0, from the tile's first block
+      const long base = KC ? (op.r0 >> 5) * blk_pitch<SZ>(op.ld)
+                           : static_cast<long>(k0 >> 5) * blk_pitch<SZ>(op.ld) + (op.r0 >> 5) * (1024 * SZ) +
+                                 (k0 & 31) * 16;
+      return make_rsrc(p + base, static_cast<uint64_t>(op.extent * SZ - base));
+    }
     if (KT) {  // rows [r0, ld) of the block of k tile k0 / BK (64 bytes per row)
       const long base = (static_cast<long>(k0 / BK) * op.ld + op.r0) * BK;
       return make_rsrc(op.ptr + base, static_cast<uint64_t>(op.ld - op.r0) * 64);
@@ -218,10 +271,12 @@ struct StageLoader {
                                         int wave) const {
     // k tiled: the buffer resource starts at the tile's block, whose k
     // padding holds zeros
-    const bool kc_ok = !KC || KT || k0 + rel_k(threadIdx.x & 63) < op.k_lim;
+    // (a blocked operand's k range is whole k tiles: no per-lane k test)
+    const bool kc_ok = !KC || KT || BL || k0 + rel_k(threadIdx.x & 63) < op.k_lim;
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
-      const uint32_t o = KC && !KT ? voff[i] + static_cast<uint32_t>(k0 * SZ) : voff[i];
+      const uint32_t o = BL ? (KC ? voff[i] + static_cast<uint32_t>((k0 >> 5) * BLK + (k0 & 31) * SZ * 32) : voff[i])
+                         : (KC && !KT ? voff[i] + static_cast<uint32_t>(k0 * SZ) : voff[i]);
       lds_dma16(rs, kc_ok ? o : kOOB, dst + static_cast<uint32_t>((wave * NI + i) * 1024));
     }
   }
@@ -232,11 +287,36 @@ struct StageLoader {
 
 // Fragment read of one operand for a wave: 32 tile rows from row0, k step
 // kk (16 k for bf16, 8 for fp32; two steps per k tile).
-template <typename T, int R, bool KC>
+template <typename T, int R, bool KC, bool BL = false>
 struct FragReader {
   static constexpr int SZ = static_cast<int>(sizeof(T));
+  static constexpr int BK = 64 / SZ;
   __device__ __forceinline__ static u32x4 read(const char* stage, int row0, int kk, int lane) {
-    if (KC) {
+    if (BL && !KC) {  // blocked stage: [R / 32][granule][BK k rows][16 B]
+      // row0 is a multiple of 32, so the lane's granule, swizzle and k rows
+      // depend on the lane alone; the block and the k step are constant offsets
+      const char* blk = stage + (row0 >> 5) * 2048;
+      if (SZ == 2) {
+        const int q = lane >> 4, s = lane & 15;
+        const int g = 2 * (q & 1) + ((s & 3) >> 1), sw = bl_swz<SZ>(g);
+        const int kl = 8 * (q >> 1) + (s >> 2);  // k row in the step, below 16: the swizzle keeps bit 4
+        const char* p0 = blk + g * (BK * 16) + 8 * (s & 1) + kk * 256;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + ((kl ^ sw) << 4)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + (((kl + 4) ^ sw) << 4)));
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+        return u32x4{a[0], a[1], b[0], b[1]};
+      } else {
+        const int h = lane >> 5, g = (lane & 31) >> 2, sw = bl_swz<SZ>(g);
+        const char* p0 = blk + g * (BK * 16) + ((lane & 3) << 2);
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = *(const lds_u32*)(p0 + (((8 * kk + 4 * h + j) ^ sw) << 4));
+        return v;
+      }
+    } else if (BL) {  // KC, blocked stage: [chunk][R rows][16 B]
+      const int c = 2 * kk + (lane >> 5);
+      return *(const lds_u32x4*)(stage + c * (R * 16) + (row0 + (lane & 31)) * 16);
+    } else if (KC) {
       const int r = row0 + (lane & 31);
       const int c = 2 * kk + (lane >> 5);
       return *(const lds_u32x4*)(stage + r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
@@ -264,12 +344,14 @@ struct FragReader {
 };
 
 // A_KT / B_KT: that operand is k tiled (KT above; requires it to be KC).
+// A_BL: A is blocked (BL above).
 // TRANS: the matrix cores take B as their first operand, so atom (i, j)
 // holds the transposed product: element e of a lane is (row 32 i + (lane &
 // 31), column 32 j + 8 (e >> 2) + 4 (lane >> 5) + (e & 3)) of the wave tile,
 // i.e. each lane holds whole groups of 4 consecutive columns of FM rows.
 template <typename T, int BM_, int BN_, bool A_KC, bool B_KC, int WAVES_M = 2, int WAVES_N = 4, int NS_ = 4,
-          bool EARLY_BARRIER = false, bool A_KT = false, bool B_KT = false, bool SPREAD = false, bool TRANS = false>
+          bool EARLY_BARRIER = false, bool A_KT = false, bool B_KT = false, bool SPREAD = false, bool TRANS = false,
+          bool A_BL = false>
 struct Gemm {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int SZ = static_cast<int>(sizeof(T));
@@ -285,9 +367,9 @@ struct Gemm {
   static constexpr int LDS_BYTES = NS * STAGE;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 
-  using LA = StageLoader<T, BM, A_KC, NWAVES, A_KT>;
+  using LA = StageLoader<T, BM, A_KC, NWAVES, A_KT, A_BL>;
   using LB = StageLoader<T, BN, B_KC, NWAVES, B_KT>;
-  using RA = FragReader<T, BM, A_KC>;
+  using RA = FragReader<T, BM, A_KC, A_BL>;
   using RB = FragReader<T, BN, B_KC>;
   static constexpr int NI = LA::NI + LB::NI;     // load instructions per wave per tile
 

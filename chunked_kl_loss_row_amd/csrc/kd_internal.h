@@ -45,9 +45,10 @@ struct ChunkArgs {
   float* ps;        // [chunk][nvt] per-tile sum of exp(z - max)
   double* rl;       // [chunk] per-row loss
   double* loss_acc; // [1] running loss
-  void* dz;         // [chunk][ldz] dZ in x dtype
+  void* dz;         // dZ of the group in x dtype, blocked: [rows rounded up to 32][ldz] (blk_offset)
+  int dz_row0;      // row of the dZ region where this chunk's rows start (single-call path)
   float* dhp;       // [split][chunk][d] split partials of dH
-  float* zc;        // [chunk][ldz] fp32 logits kept by the forward (single-call path), else null
+  float* zc;        // fp32 logits kept by the forward (single-call path), blocked like dZ, else null
   void* hk;         // H_c in k tiles of 64 bytes: [ceil(d / tile k)][ldk][tile k] (x dtype)
   int ldk;          // rows per k-tile block of hk (the chunk size)
   void* ht;         // H^T of the chunks of one dW group, k tiled: [ldt / tile k][d][tile k] (x dtype)

@@ -35,11 +35,12 @@ using ProjGemmT = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true, true, fal
 // (TRANS): its epilogue then works on whole row segments held in registers.
 template <typename T>
 using ProjGemmX = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true, true, false, true, true>;
+// dH and dW read dZ blocked (the dZ passes write it so).
 template <typename T>
-using DhGemm = Gemm<T, kDhBM, kDhBN, true, false, 2, 4, 4, true>;
+using DhGemm = Gemm<T, kDhBM, kDhBN, true, false, 2, 4, 4, true, false, false, false, false, true>;
 // dW reads H_c^T k tiled as well (k_transpose_h writes it so).
 template <typename T>
-using DwGemm = Gemm<T, kDwBM, kDwBN, false, true, 2, 4, 4, false, false, true>;
+using DwGemm = Gemm<T, kDwBM, kDwBN, false, true, 2, 4, 4, false, false, true, false, false, true>;
 static_assert(ProjGemm<uint16_t>::NT == ProjGemm<float>::NT && ProjGemmT<uint16_t>::NT == ProjGemm<uint16_t>::NT &&
                   DhGemm<uint16_t>::NT == DhGemm<float>::NT &&
                   DwGemm<uint16_t>::NT == DwGemm<float>::NT,
@@ -266,17 +267,17 @@ __global__ __launch_bounds__(512, 1) void k_fwd_proj(const T* __restrict__ hk, i
   // column in tile of element e of atom j: c0 + 32 j + 8 (e >> 2) + (e & 3)
   const int c0 = wn * G::WN + 4 * half;
   const int r0 = wm * G::WM + (lane & 31);  // row in tile of atom row i: r0 + 32 i
-  if (zc) {  // single-call path: keep the fp32 logits of the chunk
+  if (zc) {  // single-call path: keep the fp32 logits of the chunk (blocked, as dZ)
 #pragma unroll
     for (int i = 0; i < G::FM; ++i) {
       const int grow = rt * G::BM + r0 + 32 * i;
       if (grow >= rows) continue;
-      float* zrow = zc + static_cast<long>(grow) * ldz + vt * G::BN + c0;
+      char* zrow = reinterpret_cast<char*>(zc) + blk_offset<4>(grow, vt * G::BN + c0, ldz);
 #pragma unroll
       for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<f32x4*>(zrow + 32 * j + 8 * g) =
+        for (int g = 0; g < 4; ++g)  // columns c0 + 32 j + 8 g + [0, 4): one granule
+          *reinterpret_cast<f32x4*>(zrow + j * 4096 + g * 1024) =
               f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
     }
   }
@@ -455,11 +456,11 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ gptr, T* __restrict__ dz,
                                                    float t2, float tau) {
-  using G = ProjGemmT<T>;
-  __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
+  using G = ProjGemmX<T>;
+  constexpr int SZ = static_cast<int>(sizeof(T)), BLK = 1024 * SZ;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   __shared__ int s_lo[G::BM], s_hi[G::BM];
-  __shared__ float s_lse2[G::BM], s_coef[G::BM], s_gm[G::BM];
-  __shared__ int s_live[G::BM];
+  __shared__ f32x4 s_rc[G::BM];            // per row: lse log2(e), coefficient, g tau, live
   __shared__ int s_hcol[G::BM][kMaxHits];  // column in tile of the row's teacher ids here
   __shared__ float s_hp[G::BM][kMaxHits];  // their teacher probabilities
   const int rtn = (rows + G::BM - 1) / G::BM;
@@ -486,10 +487,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
     }
     s_lo[r] = lo;
     s_hi[r] = hi;
-    s_lse2[r] = lse2;
-    s_coef[r] = coef;
-    s_gm[r] = gm;
-    s_live[r] = live;
+    s_rc[r] = f32x4{lse2, coef, gm, live ? 1.f : 0.f};
     if (hi - lo <= kMaxHits)
       for (int q = lo; q < hi; ++q) {
         const long kq = static_cast<long>(gr) * K + q;
@@ -500,87 +498,90 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
   f32x16 acc[G::FM][G::FN];
   const Operand<T> A{hk, ldk, static_cast<long>((d + G::BK - 1) / G::BK) * ldk * G::BK, rt * G::BM, rows, d};
   const Operand<T> B{W, d, static_cast<long>(v) * d, vt * G::BN, v, d};
-  G::run(A, B, 0, d, smem, acc);
+  G::run(A, B, 0, d, smem, acc);  // ends with a barrier: the tables above are visible
 
-  float* stage = reinterpret_cast<float*>(smem);
-  const int g16 = tid >> 4, l16 = tid & 15;
+  // The tile is transposed in the accumulators: each lane holds rows r0 + 32 i
+  // and, per atom j, 4 groups of 4 consecutive columns, which are 8 (bf16) or
+  // 16 (fp32) contiguous bytes of dZ's blocked layout; the lanes of a store
+  // instruction cover 512 contiguous bytes.  Rows from `rows` up to a whole
+  // block are written as zeros (dW reads whole blocks of rows).
+  const int lane = tid & 63, wave = tid >> 6, wm = wave / G::WAVES_COLS, wn = wave % G::WAVES_COLS;
+  const int half = lane >> 5;
+  const int r0 = wm * G::WM + (lane & 31);
+  const int c0 = wn * G::WN + 4 * half;  // column in tile of element 4 g + e of atom j: c0 + 32 j + 8 g + e
+  const int rpad = (rows + 31) & ~31;
   const bool full_tile = (vt + 1) * G::BN <= v;
+  char* const zb = reinterpret_cast<char*>(dz);
 #pragma unroll
-  for (int h = 0; h < G::BM / kStageRows; ++h) {
-    stage_slice<G>(stage, acc, h);
-    lds_barrier();
-    for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
-      const int row = h * kStageRows + rr, grow = rt * G::BM + row;
-      if (grow >= rows) break;
-      T* out = dz + static_cast<long>(grow) * ldz + vt * G::BN;
-      if (s_live[row] == 0) {  // masked row: exact zeros, whatever its inputs hold
+  for (int i = 0; i < G::FM; ++i) {
+    const int row = r0 + 32 * i, grow = rt * G::BM + row;
+    if (grow >= rpad) continue;  // the same for the wave's 32 lanes of this row block
+    const f32x4 rc = s_rc[row];
+    const bool live = rc[3] != 0.f;
+    char* const out = zb + blk_offset<SZ>(grow, static_cast<long>(vt) * G::BN + c0, ldz);
 #pragma unroll
-        for (int jj = 0; jj < G::BN / 64; ++jj) {
-          if constexpr (sizeof(T) == 2)
-            *reinterpret_cast<uint2*>(out + jj * 64 + l16 * 4) = make_uint2(0u, 0u);
-          else
-            *reinterpret_cast<f32x4*>(out + jj * 64 + l16 * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        continue;
-      }
-      const float lse2 = s_lse2[row], coef = s_coef[row], gm = s_gm[row];
-      const int lo = s_lo[row], n = s_hi[row] - lo;
-      float o[G::BN / 64][4];
-      {
+    for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-        for (int jj = 0; jj < G::BN / 64; ++jj) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(stage + rr * kStagePitch + jj * 64 + l16 * 4);
+      for (int gq = 0; gq < 4; ++gq) {
+        float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[jj][e] = dz_exp(x[e], coef, lse2, t2);
-        }
+        for (int e = 0; e < 4; ++e) o[e] = live ? dz_exp(acc[i][j][4 * gq + e], rc[1], rc[0], t2) : 0.f;
         if (!full_tile) {  // columns past v: zero padding of dZ
 #pragma unroll
-          for (int jj = 0; jj < G::BN / 64; ++jj)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (vt * G::BN + jj * 64 + l16 * 4 + e >= v) o[jj][e] = 0.f;
+          for (int e = 0; e < 4; ++e)
+            if (vt * G::BN + c0 + 32 * j + 8 * gq + e >= v) o[e] = 0.f;
         }
-      }
-#pragma unroll
-      for (int jj = 0; jj < G::BN / 64; ++jj) {
-        const int c0 = jj * 64 + l16 * 4;
-        if constexpr (sizeof(T) == 2) {  // one nearest-even rounding per value, two per instruction
-          *reinterpret_cast<uint2*>(out + c0) = make_uint2(pack_bf16x2(o[jj][0], o[jj][1]), pack_bf16x2(o[jj][2], o[jj][3]));
+        if constexpr (SZ == 2) {  // one nearest-even rounding per value
+          *reinterpret_cast<uint2*>(out + j * BLK + gq * 512) =
+              make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         } else {
-          *reinterpret_cast<f32x4*>(out + c0) = f32x4{o[jj][0], o[jj][1], o[jj][2], o[jj][3]};
+          *reinterpret_cast<f32x4*>(out + j * BLK + gq * 1024) = f32x4{o[0], o[1], o[2], o[3]};
         }
       }
-      // The row's teacher ids in this tile: their elements are stored again
-      // with p subtracted before the single rounding, by the lane that stored
-      // the element's group of 4 columns (same thread, same address: the
-      // later store lands last).  The keys are sorted by id, so the hits of
-      // an id that repeats in the row are adjacent: the owning lane carries
-      // one fp32 value per column, subtracts each p from it in key order
-      // (the order of the cached-logit pass) and stores it after each hit,
-      // so the last store of a column holds every term.  The other elements
-      // are unchanged, so this equals subtracting p inside the row pass.
-      int prev_c = -1;
-      float run = 0.f;
-      for (int q = 0; q < n; ++q) {
-        int c;
-        float sub;
-        if (n <= kMaxHits) {
-          c = s_hcol[row][q];
-          sub = s_hp[row][q];
-        } else {
-          const long kq = static_cast<long>(grow) * K + lo + q;
-          c = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
-          sub = psort[kq];
-        }
-        if (((c >> 2) & 15) == l16) {
-          if (c != prev_c) run = dz_exp(stage[rr * kStagePitch + c], coef, lse2, t2);
-          run = dz_sub(run, sub * gm);
-          out[c] = Elem<T>::from_f32(run);
-        }
-        prev_c = c;
+  }
+  // The row's teacher ids in this tile: their elements are stored again with
+  // p subtracted before the single rounding, by the lane that stored them
+  // (same thread, same address: the later store lands last).  The keys are
+  // sorted by id, so the hits of an id that repeats in the row are adjacent:
+  // the owning lane carries one fp32 value per column, subtracts each p from
+  // it in key order (the order of the cached-logit pass) and stores it after
+  // each hit, so the last store of a column holds every term.
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i) {
+    const int row = r0 + 32 * i, grow = rt * G::BM + row;
+    const int lo = s_lo[row], n = s_hi[row] - lo;  // no hits on rows past `rows` or masked rows
+    if (n == 0) continue;
+    const f32x4 rc = s_rc[row];
+    int prev_c = -1;
+    float run = 0.f;
+    for (int q = 0; q < n; ++q) {
+      int c;
+      float sub;
+      if (n <= kMaxHits) {
+        c = s_hcol[row][q];
+        sub = s_hp[row][q];
+      } else {
+        const long kq = static_cast<long>(grow) * K + lo + q;
+        c = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
+        sub = psort[kq];
       }
+      const int cw = c - wn * G::WN;
+      if (cw >= 0 && cw < G::WN && ((cw >> 2) & 1) == half) {
+        if (c != prev_c) {
+          const int jc = cw >> 5, ec = (cw & 3) + 4 * ((cw >> 3) & 3);
+          float z = 0.f;
+#pragma unroll
+          for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) z = (j == jc && e == ec) ? acc[i][j][e] : z;
+          run = dz_exp(z, rc[1], rc[0], t2);
+        }
+        run = dz_sub(run, sub * rc[2]);
+        *reinterpret_cast<T*>(zb + blk_offset<SZ>(grow, static_cast<long>(vt) * G::BN + c, ldz)) =
+            Elem<T>::from_f32(run);
+      }
+      prev_c = c;
     }
-    lds_barrier();
   }
 }
 
@@ -590,10 +591,16 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
 // The same dZ as k_bwd_dz, bit for bit (same fp32 logits, same formula),
 // from the chunk's cached logits instead of a recomputed projection.  One
 // thread per 8 consecutive columns of a row (ldz is a multiple of the
-// projection tile width, so the 8 columns lie in one vocabulary tile).
+// projection tile width, so the 8 columns lie in one vocabulary tile); the
+// 32 threads of a block's granule run are consecutive, so both the logits
+// and dZ (both blocked) move in 512-byte runs.  The chunk's rows start at
+// row0 of the group's dZ region, which need not be a block boundary: rows
+// of the blocks it covers that belong to the chunk before are left alone,
+// rows past the chunk up to a whole block are written as zeros.
 template <typename T>
-__global__ __launch_bounds__(256) void k_dz_cached(const float* __restrict__ zc, int ldz, int rows, int v,
-                                                   int K, int nvt, const uint16_t* __restrict__ lb,
+__global__ __launch_bounds__(256) void k_dz_cached(const float* __restrict__ zc, int ldz, int row0, int rows,
+                                                   int rb0, int nrb, int v, int K, int nvt,
+                                                   const uint16_t* __restrict__ lb,
                                                    const uint32_t* __restrict__ keys,
                                                    const float* __restrict__ psort,
                                                    const float* __restrict__ ssum,
@@ -601,16 +608,24 @@ __global__ __launch_bounds__(256) void k_dz_cached(const float* __restrict__ zc,
                                                    const float* __restrict__ lse,
                                                    const float* __restrict__ gptr, T* __restrict__ dz,
                                                    float t2, float tau) {
-  const int per_row = ldz / 8;
+  constexpr int SZ = static_cast<int>(sizeof(T));
+  // thread -> (block row rb0 + q / nvb, block column q % nvb, 8-column group, row in block)
+  const int nvb = ldz / 32;
   const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<long>(rows) * per_row) return;
-  const int row = static_cast<int>(idx / per_row), c0 = static_cast<int>(idx % per_row) * 8;
+  if (idx >= static_cast<long>(nrb) * nvb * 128) return;
+  const int m = static_cast<int>(idx & 31), g8 = static_cast<int>((idx >> 5) & 3);
+  const long q = idx >> 7;
+  const int cb = static_cast<int>(q % nvb);
+  const long R = (rb0 + q / nvb) * 32 + m;  // row of the dZ region
+  if (R < row0) return;                     // an earlier chunk's row
+  const int row = static_cast<int>(R - row0), c0 = cb * 32 + g8 * 8;
   float o[8];
-  if (mask == nullptr || mask[row] != 0) {
+  if (row < rows && (mask == nullptr || mask[row] != 0)) {
     const float g = gptr ? gptr[0] : 1.f;
     const float lse2 = lse[row] * kLog2e, coef = g * ssum[row] * tau, gt = g * tau;
-    const f32x4 z0 = *reinterpret_cast<const f32x4*>(zc + static_cast<long>(row) * ldz + c0);
-    const f32x4 z1 = *reinterpret_cast<const f32x4*>(zc + static_cast<long>(row) * ldz + c0 + 4);
+    const char* zr = reinterpret_cast<const char*>(zc) + blk_offset<4>(row, c0, ldz);
+    const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr);
+    const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + 512);  // columns c0 + 4..7: the next granule
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       o[e] = dz_exp(z0[e], coef, lse2, t2);
@@ -618,8 +633,8 @@ __global__ __launch_bounds__(256) void k_dz_cached(const float* __restrict__ zc,
     }
     const int t = c0 / kProjBN;
     const int lo = lb[static_cast<long>(row) * (nvt + 1) + t], hi = lb[static_cast<long>(row) * (nvt + 1) + t + 1];
-    for (int q = lo; q < hi; ++q) {
-      const long kq = static_cast<long>(row) * K + q;
+    for (int qq = lo; qq < hi; ++qq) {
+      const long kq = static_cast<long>(row) * K + qq;
       const int c = static_cast<int>(keys[kq] >> 8) - c0;
       if (static_cast<unsigned>(c) < 8u) {
         const float sub = psort[kq] * gt;
@@ -632,17 +647,17 @@ __global__ __launch_bounds__(256) void k_dz_cached(const float* __restrict__ zc,
       for (int e = 0; e < 8; ++e)
         if (c0 + e >= v) o[e] = 0.f;
     }
-  } else {
+  } else {  // masked rows, and rows past the chunk up to a whole block: zeros
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
   }
-  T* out = dz + static_cast<long>(row) * ldz + c0;
-  if constexpr (sizeof(T) == 2) {
+  char* out = reinterpret_cast<char*>(dz) + blk_offset<SZ>(R, c0, ldz);
+  if constexpr (SZ == 2) {
     *reinterpret_cast<uint4*>(out) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
                                                 pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
   } else {
     *reinterpret_cast<f32x4*>(out) = f32x4{o[0], o[1], o[2], o[3]};
-    *reinterpret_cast<f32x4*>(out + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    *reinterpret_cast<f32x4*>(out + 512) = f32x4{o[4], o[5], o[6], o[7]};
   }
 }
 
@@ -664,7 +679,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dh(const T* __restrict__ dz, int
   const int k0 = ks * kslice, k1 = min(ldz, k0 + kslice);
   f32x16 acc[G::FM][G::FN];
   // A(m = chunk row, k = vocab) = dZ[m][k];  B(n = hidden, k = vocab) = W[k][n]
-  const Operand<T> A{dz, ldz, static_cast<long>(rows) * ldz, mt * G::BM, rows, ldz};
+  const Operand<T> A{dz, ldz, (rows + 31) / 32 * blk_pitch<sizeof(T)>(ldz) / static_cast<long>(sizeof(T)), mt * G::BM,
+                     rows, ldz};
   const Operand<T> B{W, d, static_cast<long>(v) * d, nt * G::BN, d, v};
   G::run(A, B, k0, k1, smem, acc);
   // rows past the chunk fall outside the region; columns past d get kOOB
@@ -812,7 +828,10 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
   if (t < 0) return;
   const int mt = t / ntn, nt = t % ntn;
   // A(m = vocab, k = chunk row) = dZ[k][m];  B(n = hidden, k = chunk row) = H_c^T[n][k]
-  const Operand<T> A{dz, ldz, static_cast<long>(rows) * ldz, mt * G::BM, ldz, rows};
+  // dZ's rows past `rows` are zero up to a whole block, so k tiles that run
+  // past `rows` read zeros there
+  const Operand<T> A{dz, ldz, (rows + 31) / 32 * blk_pitch<sizeof(T)>(ldz) / static_cast<long>(sizeof(T)), mt * G::BM,
+                     ldz, rows};
   const Operand<T> B{ht, d, static_cast<long>(d) * ldt, nt * G::BN, d, rows};
   // dW += dZ^T H_c with the accumulators starting from the tile's current dW
   // values: they are loaded while the first operand tiles are in flight and
@@ -1129,27 +1148,24 @@ void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStre
 }
 
 void launch_dz_cached(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s) {
-  // One thread per 8 columns; the chunk goes in row slices of at most 2^31
-  // threads (a launch's work-item count must fit in 32 bits).
-  const long per_row = a.ldz / 8;
-  const long slice = (1L << 31) / per_row;
-  const size_t xs = a.x_bf16 ? 2 : 4;
-  for (long r0 = 0; r0 < a.rows; r0 += slice) {
-    const int rows = static_cast<int>(a.rows - r0 < slice ? a.rows - r0 : slice);
-    const long threads = rows * per_row;
+  // One thread per 8 columns of a row of the block rows the chunk touches;
+  // those go in slices of at most 2^31 threads (a launch's work-item count
+  // must fit in 32 bits).
+  const long per_rb = static_cast<long>(a.ldz) / 32 * 128;  // threads per block row
+  const long slice = (1L << 31) / per_rb;
+  const long rb_first = a.dz_row0 / 32, rb_end = (static_cast<long>(a.dz_row0) + a.rows + 31) / 32;
+  for (long rb = rb_first; rb < rb_end; rb += slice) {
+    const int nrb = static_cast<int>(rb_end - rb < slice ? rb_end - rb : slice);
+    const long threads = nrb * per_rb;
     const dim3 grid(static_cast<unsigned>((threads + 255) / 256)), block(256);
-    const long zo = r0 * a.ldz, ko = r0 * a.k;
-    const uint16_t* lb = a.lb + r0 * (a.nvt + 1);
-    const uint8_t* mask = a.mask ? a.mask + r0 : nullptr;
-    void* dz = static_cast<char*>(a.dz) + static_cast<size_t>(zo) * xs;
     if (a.x_bf16)
-      k_dz_cached<uint16_t><<<grid, block, 0, s>>>(a.zc + zo, a.ldz, rows, a.v, a.k, a.nvt, lb, a.keys + ko,
-                                                   a.psort + ko, a.ssum + r0, mask, lse + r0, g,
-                                                   static_cast<uint16_t*>(dz), kLog2e / a.tau, a.tau);
+      k_dz_cached<uint16_t><<<grid, block, 0, s>>>(a.zc, a.ldz, a.dz_row0, a.rows, static_cast<int>(rb), nrb, a.v,
+                                                   a.k, a.nvt, a.lb, a.keys, a.psort, a.ssum, a.mask, lse, g,
+                                                   static_cast<uint16_t*>(a.dz), kLog2e / a.tau, a.tau);
     else
-      k_dz_cached<float><<<grid, block, 0, s>>>(a.zc + zo, a.ldz, rows, a.v, a.k, a.nvt, lb, a.keys + ko,
-                                                a.psort + ko, a.ssum + r0, mask, lse + r0, g,
-                                                static_cast<float*>(dz), kLog2e / a.tau, a.tau);
+      k_dz_cached<float><<<grid, block, 0, s>>>(a.zc, a.ldz, a.dz_row0, a.rows, static_cast<int>(rb), nrb, a.v,
+                                                a.k, a.nvt, a.lb, a.keys, a.psort, a.ssum, a.mask, lse, g,
+                                                static_cast<float*>(a.dz), kLog2e / a.tau, a.tau);
   }
 }
 

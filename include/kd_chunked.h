@@ -151,7 +151,8 @@ int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace kd_chunked_fwd_bwd needs for `prob`: the fwd/bwd
- * workspace plus one chunk of fp32 logits (chunk x 384*ceil(v/384) floats).
+ * workspace plus one chunk of fp32 logits (chunk rounded up to 32 rows, x
+ * 384*ceil(v/384) floats, plus 256 bytes per 32 rows).
  * Independent of n.  Returns 0 for an invalid problem. */
 size_t kd_chunked_fwd_bwd_workspace_size(const kd_problem* prob);
 
