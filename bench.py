@@ -55,8 +55,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=3072, help="rows of the CPU oracle sample (about 15-20 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
-                    help="rocprofv3 FETCH_SIZE/WRITE_SIZE summary of the dominant kernel "
-                         "(default: profiles/kd_<kernel>_<workload>_traffic.txt)")
+                    help="rocprofv3 FETCH_SIZE/WRITE_SIZE summary with a line per matrix-core kernel "
+                         "(default: profiles/kd_gemms_<workload>_traffic.txt)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip timing the single-call variant (kd_chunked_fwd_bwd)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -80,22 +80,27 @@ def source_digest():
 
 
 def read_traffic(path, kernel):
-    """HBM bytes per launch from a committed counter summary, or None when it is missing,
-    names another kernel or was taken on other kernel sources."""
+    """HBM bytes per launch of ``kernel`` from a committed counter summary (lines
+    ``traffic: <kernel> <scaled bytes per launch>`` under ``source_digest: <digest>``),
+    or None when the summary is missing, has no line for the kernel or was taken on
+    other kernel sources."""
     if not path or not os.path.exists(path):
         return None
-    fields = {}
+    digest, found = None, None
     with open(path) as f:
         for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, _, v = line.partition(":")
-                fields[k.strip()] = v.strip()
-    if fields.get("kernel") != kernel or fields.get("source_digest") != source_digest():
-        return None
-    try:
-        return int(float(fields["scaled_bytes_per_launch"]))
-    except (KeyError, ValueError):
-        return None
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.split()
+            if k == "source_digest" and v:
+                digest = v[0]
+            elif k == "traffic" and len(v) >= 2 and v[0] == kernel:
+                try:
+                    found = int(float(v[1]))
+                except ValueError:
+                    return None
+    return found if digest == source_digest() else None
 
 
 def read_clock(path, kernel):
@@ -277,7 +282,7 @@ def main():
         per_launch_flop = 2.0 * N * D * V / (kern[dom][1] / args.steps)
         avg_s = kern[dom][0] / kern[dom][1] * 1e-3
         ach = per_launch_flop / avg_s / 1e12
-        tpath = args.traffic or os.path.join(ROOT, "profiles", f"kd_{dom}_{wl.name}_traffic.txt")
+        tpath = args.traffic or os.path.join(ROOT, "profiles", f"kd_gemms_{wl.name}_traffic.txt")
         traffic = read_traffic(tpath, dom)
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,

@@ -29,7 +29,7 @@ def test_more_than_one_gpu_is_refused():
 def _summary(tmp_path, kernel, digest, nbytes=123456789):
     p = tmp_path / "traffic.txt"
     p.write_text("# comment: ignored\n"
-                 f"kernel: {kernel}\nsource_digest: {digest}\nscaled_bytes_per_launch: {nbytes}\n")
+                 f"source_digest: {digest}\ntraffic: {kernel} {nbytes}\ntraffic: other_kernel 42\n")
     return str(p)
 
 
