@@ -14,8 +14,8 @@ work-items.  These tests run the path at those limits:
     at one wave per row).
 
 Rows are checked on seeded samples (the oracle evaluated on exactly those
-rows), dW on vocabulary rows summed over all positions from the GPU's lse
-(checked on the sampled rows first).  Tolerances as in the parity tests: fp32 1e-5, bf16 loss 1e-3 and gradients
+rows), dW on vocabulary rows summed over all positions from the oracle's own
+lse of every row.  Tolerances as in the parity tests: fp32 1e-5, bf16 loss 1e-3 and gradients
 1e-2 relative Frobenius; lse 1e-5 relative.
 """
 import math
