@@ -306,8 +306,13 @@ struct FragReader {
         const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
         return u32x4{a[0], a[1], b[0], b[1]};
       } else {
-        const int h = lane >> 5, g = (lane & 31) >> 2, sw = bl_swz<SZ>(g);
-        const char* p0 = blk + g * (BK * 16) + ((lane & 3) << 2);
+        // the k row offsets differ per lane in their low bits (8 per lane); an
+        // opaque copy of the lane id keeps the compiler from holding all 8 in
+        // registers across the k loop (the fp32 dW kernel has none to spare)
+        int ln;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+        const int h = ln >> 5, g = (ln & 31) >> 2, sw = bl_swz<SZ>(g);
+        const char* p0 = blk + g * (BK * 16) + ((ln & 3) << 2);
         u32x4 v;
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = *(const lds_u32*)(p0 + (((8 * kk + 4 * h + j) ^ sw) << 4));

@@ -71,14 +71,21 @@ def test_grouped_dw_keeps_prior_contents():
     torch.testing.assert_close(acc, prior + base, rtol=1e-5, atol=1e-5)
 
 
-@pytest.mark.parametrize("xd", ["bf16", "f32"])
-def test_single_call_grouped_equals_two_call(xd):
-    wl = inputs.custom(900, 136, 2500, 40, 128, x_dtype=xd, mask="random:40", tag=960)
-    d = upload(inputs.make_inputs(wl, seed=10))
-    log(f"case single-call grouped {xd}")
-    loss2, lse2, dH2, dW2 = _run(d, 128, 3)
+# chunk 100: the chunks of a group start inside dZ's 32-row blocks (the
+# single-call path writes each chunk's dZ rows after the previous chunk's)
+@pytest.mark.parametrize("xd,chunk", [("bf16", 128), ("f32", 128), ("bf16", 100), ("f32", 100)])
+def test_single_call_grouped_equals_two_call(xd, chunk):
+    wl = inputs.custom(900, 136, 2500, 40, chunk, x_dtype=xd, mask="random:40", tag=960)
+    inp = inputs.make_inputs(wl, seed=10)
+    d = upload(inp)
+    log(f"case single-call grouped {xd} chunk={chunk}")
+    loss2, lse2, dH2, dW2 = _run(d, chunk, 3)
     gl = torch.tensor([0.37], dtype=torch.float32, device="cuda")
-    one = L.forward_backward(d["H"], d["W"], d["t_ids"], d["t_logits"], d["mask"], gl, chunk=128, dw_chunks=3)
+    one = L.forward_backward(d["H"], d["W"], d["t_ids"], d["t_logits"], d["mask"], gl, chunk=chunk, dw_chunks=3)
     torch.cuda.synchronize()
     assert float(one["loss"].item()) == loss2 and torch.equal(one["lse"], lse2)
     assert torch.equal(one["dH"], dH2) and torch.equal(one["dW"], dW2)
+    ref = oracle.run(inp, g=0.37)
+    tol = 1e-5 if xd == "f32" else 1e-2
+    assert rel_fro(one["dW"].cpu().numpy(), ref["dW"]) <= tol
+    assert rel_fro(one["dH"].cpu().numpy(), ref["dH"]) <= tol
