@@ -459,10 +459,12 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
   using G = ProjGemmX<T>;
   constexpr int SZ = static_cast<int>(sizeof(T)), BLK = 1024 * SZ;
   __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
-  __shared__ int s_lo[G::BM], s_hi[G::BM];
+  __shared__ int2 s_range[G::BM];          // the row's keys in this tile: [lo, hi)
   __shared__ f32x4 s_rc[G::BM];            // per row: lse log2(e), coefficient, g tau, live
   __shared__ int s_hcol[G::BM][kMaxHits];  // column in tile of the row's teacher ids here
   __shared__ float s_hp[G::BM][kMaxHits];  // their teacher probabilities
+  __shared__ u32x4 s_hmask[G::BM];         // groups of 4 columns of the tile holding a teacher id (96 bits)
+  static_assert(G::BN == 384, "the group mask covers 96 groups of 4 columns");
   const int rtn = (rows + G::BM - 1) / G::BM;
   const int t = xcd_tile(blockIdx.x, rtn * nvt);
   if (t < 0) return;
@@ -485,15 +487,19 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
         coef = g * ssum[gr] * tau;  // g and tau folded into the row coefficient
       }
     }
-    s_lo[r] = lo;
-    s_hi[r] = hi;
+    s_range[r] = make_int2(lo, hi);
     s_rc[r] = f32x4{lse2, coef, gm, live ? 1.f : 0.f};
-    if (hi - lo <= kMaxHits)
-      for (int q = lo; q < hi; ++q) {
-        const long kq = static_cast<long>(gr) * K + q;
-        s_hcol[r][q - lo] = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
+    uint32_t hm[3] = {0u, 0u, 0u};
+    for (int q = lo; q < hi; ++q) {
+      const long kq = static_cast<long>(gr) * K + q;
+      const int c = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
+      if (hi - lo <= kMaxHits) {
+        s_hcol[r][q - lo] = c;
         s_hp[r][q - lo] = psort[kq];
       }
+      hm[c >> 7] |= 1u << ((c >> 2) & 31);
+    }
+    s_hmask[r] = u32x4{hm[0], hm[1], hm[2], 0u};
   }
   f32x16 acc[G::FM][G::FN];
   const Operand<T> A{hk, ldk, static_cast<long>((d + G::BK - 1) / G::BK) * ldk * G::BK, rt * G::BM, rows, d};
@@ -519,6 +525,15 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
     const f32x4 rc = s_rc[row];
     const bool live = rc[3] != 0.f;
     char* const out = zb + blk_offset<SZ>(grow, static_cast<long>(vt) * G::BN + c0, ldz);
+    // The lane's groups of 4 columns are c0 / 4 + 8 j + 2 gq: bit 8 j + 2 gq of x
+    // (c0 / 4 = 24 wn + half; the 96-bit mask read as the 64 bits that hold them).
+    uint32_t x;
+    {
+      const u32x4 hm = s_hmask[row];
+      const uint64_t pr = wn < 2 ? (static_cast<uint64_t>(hm[1]) << 32 | hm[0])
+                                 : (static_cast<uint64_t>(hm[2]) << 32 | hm[1]);
+      x = static_cast<uint32_t>(pr >> ((c0 >> 2) - (wn < 2 ? 0 : 32)));
+    }
 #pragma unroll
     for (int j = 0; j < G::FN; ++j)
 #pragma unroll
@@ -531,6 +546,29 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
           for (int e = 0; e < 4; ++e)
             if (vt * G::BN + c0 + 32 * j + 8 * gq + e >= v) o[e] = 0.f;
         }
+        if ((x >> (8 * j + 2 * gq)) & 1u) {  // a teacher id in these 4 columns: its p, before the rounding
+          const int cg = c0 + 32 * j + 8 * gq;
+          const int2 rg = s_range[row];
+          const int n = rg.y - rg.x;
+          for (int q = 0; q < n; ++q) {  // key order: the p of a repeated id one after the other
+            int c;
+            float sub;
+            if (n <= kMaxHits) {
+              c = s_hcol[row][q];
+              sub = s_hp[row][q];
+            } else {
+              const long kq = static_cast<long>(grow) * K + rg.x + q;
+              c = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
+              sub = psort[kq];
+            }
+            const int dc = c - cg;
+            if (static_cast<unsigned>(dc) < 4u) {
+              const float sg = sub * rc[2];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = dz_sub(o[e], dc == e ? sg : 0.f);
+            }
+          }
+        }
         if constexpr (SZ == 2) {  // one nearest-even rounding per value
           *reinterpret_cast<uint2*>(out + j * BLK + gq * 512) =
               make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
@@ -538,50 +576,6 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dz(const T* __restrict__ hk, int
           *reinterpret_cast<f32x4*>(out + j * BLK + gq * 1024) = f32x4{o[0], o[1], o[2], o[3]};
         }
       }
-  }
-  // The row's teacher ids in this tile: their elements are stored again with
-  // p subtracted before the single rounding, by the lane that stored them
-  // (same thread, same address: the later store lands last).  The keys are
-  // sorted by id, so the hits of an id that repeats in the row are adjacent:
-  // the owning lane carries one fp32 value per column, subtracts each p from
-  // it in key order (the order of the cached-logit pass) and stores it after
-  // each hit, so the last store of a column holds every term.
-#pragma unroll
-  for (int i = 0; i < G::FM; ++i) {
-    const int row = r0 + 32 * i, grow = rt * G::BM + row;
-    const int lo = s_lo[row], n = s_hi[row] - lo;  // no hits on rows past `rows` or masked rows
-    if (n == 0) continue;
-    const f32x4 rc = s_rc[row];
-    int prev_c = -1;
-    float run = 0.f;
-    for (int q = 0; q < n; ++q) {
-      int c;
-      float sub;
-      if (n <= kMaxHits) {
-        c = s_hcol[row][q];
-        sub = s_hp[row][q];
-      } else {
-        const long kq = static_cast<long>(grow) * K + lo + q;
-        c = static_cast<int>(keys[kq] >> 8) - vt * G::BN;
-        sub = psort[kq];
-      }
-      const int cw = c - wn * G::WN;
-      if (cw >= 0 && cw < G::WN && ((cw >> 2) & 1) == half) {
-        if (c != prev_c) {
-          const int jc = cw >> 5, ec = (cw & 3) + 4 * ((cw >> 3) & 3);
-          float z = 0.f;
-#pragma unroll
-          for (int j = 0; j < G::FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) z = (j == jc && e == ec) ? acc[i][j][e] : z;
-          run = dz_exp(z, rc[1], rc[0], t2);
-        }
-        run = dz_sub(run, sub * rc[2]);
-        *reinterpret_cast<T*>(zb + blk_offset<SZ>(grow, static_cast<long>(vt) * G::BN + c, ldz)) =
-            Elem<T>::from_f32(run);
-      }
-      prev_c = c;
-    }
   }
 }
 
