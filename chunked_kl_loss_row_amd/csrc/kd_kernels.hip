@@ -3,16 +3,21 @@
 // Per chunk of rows (the pages' "one chunk of the sequence at a time":
 // agentlenshq.com page "LLMのための効率的な知識蒸留…", section
 // "2. Fused Chunked KL Loss"):
-//   forward : k_prep -> k_fwd_proj -> k_merge -> k_loss_fold
-//   backward: k_prep -> k_bwd_dz -> k_bwd_dh (+ k_dh_reduce) -> k_bwd_dw
-//   single call (forward + backward): k_prep -> k_fwd_proj keeping the
-//             chunk's fp32 logits -> k_merge -> k_loss_fold -> k_dz_cached
-//             -> k_bwd_dh (+ k_dh_reduce) -> k_bwd_dw
+//   forward (passes of up to 8 chunks): k_prep -> k_tile_h -> k_fwd_proj ->
+//             k_merge -> k_loss_fold
+//   backward (groups of dw_chunks chunks): k_prep -> k_tile_h -> k_bwd_dz ->
+//             k_bwd_dh (+ k_dh_reduce) -> k_transpose_h -> k_bwd_dw
+//   single call (forward + backward), per chunk: k_prep -> k_tile_h ->
+//             k_fwd_proj keeping the chunk's fp32 logits -> k_merge ->
+//             k_loss_fold -> k_dz_cached -> k_transpose_h; per group:
+//             k_bwd_dh (+ k_dh_reduce) -> k_bwd_dw
 //   teacher top-K producer: k_topk_pass<0> (sampled row maxima) ->
-//             k_topk_threshold -> k_topk_pass<1> (candidates) -> k_topk_select
-// The per-chunk logit tile lives only in registers / LDS in the forward; in
-// the backward the closed-form dZ of one chunk is written to the workspace
-// (bounded by the chunk size) and consumed by the two gradient GEMMs.
+//             k_topk_threshold(_reg) -> k_topk_pass<1> (candidates) ->
+//             k_topk_select
+// The logit tile lives only in registers in the forward (the projections
+// hold it transposed in the accumulators); in the backward the closed-form
+// dZ of one group of chunks is written to the workspace in 32 x 32 blocks
+// (bounded by the group's rows) and consumed by the two gradient GEMMs.
 #include <math.h>
 
 #include "kd_gemm.h"
