@@ -452,7 +452,7 @@ int kd_chunked_bwd(const kd_problem* prob, const void* H, const void* W, const i
   if (st != KD_OK) return st;
   const kd_problem& p = *prob;
   if (p.n > 0 && (!H || !W || !t_ids || !t_logits || !lse || !dH || !dW || !workspace)) return KD_ERR_NULL;
-  if (p.n > 0 && (!aligned16(H) || !aligned16(W) || !aligned16(dH))) return KD_ERR_ALIGN;
+  if (p.n > 0 && (!aligned16(H) || !aligned16(W) || !aligned16(dH) || !aligned16(dW))) return KD_ERR_ALIGN;
   if (p.n > 0 && workspace_bytes < kd_chunked_workspace_size(prob)) return KD_ERR_WORKSPACE;
   st = check_device();
   if (st != KD_OK) return st;
@@ -498,7 +498,7 @@ int kd_chunked_fwd_bwd(const kd_problem* prob, const void* H, const void* W, con
   const kd_problem& p = *prob;
   if (!loss) return KD_ERR_NULL;
   if (p.n > 0 && (!H || !W || !t_ids || !t_logits || !lse || !dH || !dW || !workspace)) return KD_ERR_NULL;
-  if (p.n > 0 && (!aligned16(H) || !aligned16(W) || !aligned16(dH))) return KD_ERR_ALIGN;
+  if (p.n > 0 && (!aligned16(H) || !aligned16(W) || !aligned16(dH) || !aligned16(dW))) return KD_ERR_ALIGN;
   if (p.n > 0 && workspace_bytes < kd_chunked_fwd_bwd_workspace_size(prob)) return KD_ERR_WORKSPACE;
   st = check_device();
   if (st != KD_OK) return st;

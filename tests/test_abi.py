@@ -92,6 +92,10 @@ def test_bad_dtype_and_alignment():
     st = B.kd_chunked_bwd(P(), fake, fake, fake, fake, None, fake, None, fake + 4, fake,
                           workspace=fake, workspace_bytes=1 << 40, stream=0, check=False)
     assert st == B.KD_ERR_ALIGN
+    # dW is read and written 16 bytes at a time
+    st = B.kd_chunked_bwd(P(), fake, fake, fake, fake, None, fake, None, fake, fake + 4,
+                          workspace=fake, workspace_bytes=1 << 40, stream=0, check=False)
+    assert st == B.KD_ERR_ALIGN
 
 
 def test_null_pointers():
