@@ -103,6 +103,71 @@ def read_traffic(path, kernel):
     return found if digest == source_digest() else None
 
 
+def parse_sclk(text):
+    """Current shader clock in MHz from the text of pp_dpm_sclk (the line marked
+    with '*'), or None."""
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            part = line.split(":", 1)[-1].strip().rstrip("*").strip().lower()
+            if part.endswith("mhz"):
+                try:
+                    return float(part[:-3])
+                except ValueError:
+                    return None
+    return None
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (pp_dpm_sclk in sysfs) from a
+    background thread while the timed steps run.  At this load the chip is
+    power-limited, so the clock it sustains differs from box to box; the
+    sampled mean is reported next to the step time as context."""
+
+    def __init__(self, period_s=0.025):
+        self.path = self._find()
+        self.period_s = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    @staticmethod
+    def _find():
+        import glob
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        return cards[0] if len(cards) == 1 else None  # several GPUs: which one is ours is not checked
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                with open(self.path) as f:
+                    mhz = parse_sclk(f.read())
+                if mhz:
+                    self.samples.append(mhz)
+            except OSError:
+                return
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        import threading
+        if self.path:
+            self._stop = threading.Event()
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"mean": round(sum(self.samples) / len(self.samples), 1), "min": min(self.samples),
+                "max": max(self.samples), "samples": len(self.samples), "source": self.path}
+
+
 def read_clock(path, kernel):
     """Shader clock (GHz) of ``kernel`` from a committed SQ-counter summary
     (rows ``kernel dur_ms cycles clk_GHz ...``), or None when the summary is
@@ -229,12 +294,14 @@ def main():
     # per-step times for the median / min next to the mean over the timed region
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        step()
-        marks[i].record(stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        e0.record(stream)
+        for i in range(args.steps):
+            step()
+            marks[i].record(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    sclk = clock.summary()
     ms = e0.elapsed_time(e1) / args.steps
     per_step = sorted([e0.elapsed_time(marks[0])] +
                       [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)])
@@ -292,6 +359,9 @@ def main():
         clk = read_clock(os.path.join(ROOT, "profiles", f"kd_gemms_{wl.name}_sq_counters.txt"), dom)
         roofline["profiled_clock_ghz"] = clk
         roofline["frac_at_profiled_clock"] = round(ach / (peak * clk / 2.4), 4) if clk else None
+        # the same against the peak at the shader clock sampled during this run's timed steps
+        # (a step average over all kernels)
+        roofline["frac_at_observed_clock"] = round(ach / (peak * sclk["mean"] / 2400.0), 4) if sclk else None
 
     variants = None
     if not args.no_variants:
@@ -431,6 +501,10 @@ def main():
                    "dw_chunks": args.dw_chunks, "mask": wl.mask, "ids": wl.ids, "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2),
         "pct_peak": round(100.0 * tflops / peak, 2),
+        # shader clock sampled during the timed steps (MHz; the rated peak assumes 2400) and the
+        # step's rate against the peak at that clock
+        "observed_sclk_mhz": sclk,
+        "pct_peak_at_observed_clock": round(100.0 * tflops / (peak * sclk["mean"] / 2400.0), 2) if sclk else None,
         "peak_gib": round(peak_gib, 3),
         "profiled_ms_per_step": round(profiled_ms, 4),
         "loss": loss_v,

@@ -7,7 +7,8 @@
 * the projection tile width used for the memory-bound passes' byte counts is
   the kernels' own;
 * the profiled clock of the dominant kernel is read only for the current
-  kernel sources.
+  kernel sources;
+* the sampled shader clock is parsed from pp_dpm_sclk's current (starred) line.
 """
 import os
 import subprocess
@@ -64,3 +65,13 @@ def test_clock_read_only_for_current_sources(tmp_path):
     assert bench.read_clock(str(p), "bwd_dh") is None
     p.write_text("source_digest: 0000000000000000\n  bwd_dw 2.5 4.7e6 1.932 2.4e6\n")
     assert bench.read_clock(str(p), "bwd_dw") is None
+
+
+def test_sclk_parse():
+    assert bench.parse_sclk("0: 500Mhz\n1: 1795Mhz *\n2: 2400Mhz\n") == 1795.0
+    assert bench.parse_sclk("0: 500Mhz *\n1: 2400Mhz\n") == 500.0
+    assert bench.parse_sclk("0: 500Mhz\n1: 2400Mhz\n") is None
+    assert bench.parse_sclk("") is None
+    with bench.ClockSampler() as c:   # no GPU here: no sysfs entry, or an idle reading
+        pass
+    assert c.summary() is None or c.summary()["samples"] >= 1
