@@ -57,11 +57,16 @@ SMALL = [
     (257, 200, 777, 256, 100, "bf16", "none"),
     (1024, 384, 5000, 100, 512, "f32", "random:100"),
     (600, 520, 2000, 64, 256, "bf16", "random:40"),
-    # hidden sizes where dW takes 256 x 320 tiles (they pad d less than 384 x 256 tiles):
-    # whole 320-wide tiles, and a partly filled last one
+    # hidden sizes spanning several dW (256-wide) and dH (384-wide) hidden tiles,
+    # the last whole or partly filled
     (450, 640, 3001, 50, 200, "f32", "random:30"),
     (333, 960, 2500, 64, 333, "bf16", "none"),
     (260, 1560, 1100, 40, 130, "f32", "tail:20"),
+    # the smallest hidden size, and a vocabulary narrower than one wave's 96 columns
+    # (three of the four waves of every projection tile hold no column below v)
+    (100, 8, 50, 8, 32, "bf16", "random:10"),
+    # every vocabulary entry is a teacher id (K = V): the -p terms cover the whole row
+    (70, 16, 96, 96, 7, "f32", "none"),
 ]
 
 
@@ -279,3 +284,22 @@ def test_ids_outside_the_vocabulary_match_nothing(xd):
     torch.cuda.synchronize()
     assert float(one["loss"].item()) == out["loss"]
     assert torch.equal(one["dH"], out["dH"]) and torch.equal(one["dW"], out["dW"])
+
+
+@pytest.mark.parametrize("xd", ["f32", "bf16"])
+def test_single_entry_vocabulary(xd):
+    """V = K = 1: the student and the renormalised teacher are both the point
+    mass, so the loss, dZ (Σp·softmax(z) - p = 1 - 1), dH and the dW added are
+    0 (the oracle's exactly; the GPU's to fp32 rounding of exp and log near 1:
+    a few units in the last place of |z| per row); lse is the single logit."""
+    wl = inputs.custom(100, 8, 1, 1, 32, x_dtype=xd, mask="random:10", tag=330)
+    inp = inputs.make_inputs(wl, seed=3)
+    log(f"case single-entry vocabulary {xd}")
+    out = run_hip(upload(inp), 32, g=0.37)
+    ref = oracle.run(inp, g=0.37)
+    assert ref["loss"] == 0.0 and np.all(ref["row_loss"] == 0.0)
+    zmax = float(np.abs(ref["lse"]).max()) + 1.0
+    assert np.abs(out["row_loss"]).max() <= 1e-6 * zmax
+    assert abs(out["loss"]) <= wl.n * 1e-6 * zmax
+    assert out["dH"].abs().max().item() <= 1e-6 and out["dW"].abs().max().item() <= 1e-5
+    np.testing.assert_allclose(out["lse"], ref["lse"], rtol=1e-5, atol=0)
