@@ -27,17 +27,13 @@
 namespace kd {
 
 // Block tiles: 256 x 384 (projection, dH) and 384 x 256 (dW), eight waves.
-// The projection keeps three LDS stages: its epilogue tables need the room.
-template <typename T>
-using ProjGemm = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true>;
-// The loss projections read H_c through its k-tiled copy (k_tile_h): every
-// 128-byte line of it a load touches is read whole.  Their tile loads go out
-// in slices between the MFMA rows (SPREAD: measured faster for these, slower
-// for dH and dW).
-template <typename T>
-using ProjGemmT = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true, true, false, true>;
-// The forward projection takes its tile transposed in the accumulators
-// (TRANS): its epilogue then works on whole row segments held in registers.
+// The projections (forward, dZ, teacher top-K) keep three LDS stages (their
+// epilogue tables need part of the rest), read H_c through its k-tiled copy
+// (k_tile_h: every 128-byte line of it a load touches is read whole), issue
+// their tile loads in slices between the MFMA rows (SPREAD: measured faster
+// for these, slower for dH and dW) and take the tile transposed in the
+// accumulators (TRANS: the epilogues work on whole row segments held in
+// registers).
 template <typename T>
 using ProjGemmX = Gemm<T, kProjBM, kProjBN, true, true, 2, 4, 3, true, true, false, true, true>;
 // dH and dW read dZ blocked (the dZ passes write it so).
@@ -46,17 +42,11 @@ using DhGemm = Gemm<T, kDhBM, kDhBN, true, false, 2, 4, 4, true, false, false, f
 // dW reads H_c^T k tiled as well (k_transpose_h writes it so).
 template <typename T>
 using DwGemm = Gemm<T, kDwBM, kDwBN, false, true, 2, 4, 4, false, false, true, false, false, true>;
-static_assert(ProjGemm<uint16_t>::NT == ProjGemm<float>::NT && ProjGemmT<uint16_t>::NT == ProjGemm<uint16_t>::NT &&
-                  DhGemm<uint16_t>::NT == DhGemm<float>::NT &&
+static_assert(ProjGemmX<uint16_t>::NT == ProjGemmX<float>::NT && DhGemm<uint16_t>::NT == DhGemm<float>::NT &&
                   DwGemm<uint16_t>::NT == DwGemm<float>::NT,
               "one block size per kernel for both dtypes");
 
-constexpr int kStageRows = 64;            // rows of the fp32 epilogue stage
-constexpr int kMaxHits = 4;               // teacher ids per (row, tile) kept in LDS; more take the slow path
-constexpr int kStagePitch = kProjBN + 8;  // floats per stage row (rows 4 apart hit other banks)
-constexpr int kStageBytes = kStageRows * kStagePitch * 4;
-template <class G>
-constexpr int proj_smem_bytes() { return G::LDS_BYTES > kStageBytes ? G::LDS_BYTES : kStageBytes; }
+constexpr int kMaxHits = 4;  // teacher ids per (row, tile) kept in LDS; more take the slow path
 
 // ---------------------------------------------------------------------------
 // teacher record -> renormalised distribution, id-sorted keys, tile ranges
@@ -183,24 +173,6 @@ __device__ __forceinline__ float dz_exp(float z, float coef, float lse2, float t
 __device__ __forceinline__ float dz_sub(float o, float sub) {
 #pragma clang fp contract(off)
   return o - sub;
-}
-
-// Write the accumulators of the rows in stage slice `h` (kStageRows rows) to
-// the fp32 stage.
-template <typename G>
-__device__ __forceinline__ void stage_slice(float* stage, const f32x16 (&acc)[G::FM][G::FN], int h) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / (G::BN / G::WN), wn = wave % (G::BN / G::WN);
-#pragma unroll
-  for (int i = 0; i < G::FM; ++i) {
-    if ((wm * G::WM + 32 * i) / kStageRows != h) continue;
-#pragma unroll
-    for (int j = 0; j < G::FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        stage[(acc_row<G>(wm, i, e, lane) - h * kStageRows) * kStagePitch + acc_col<G>(wn, j, lane)] =
-            acc[i][j][e];
-  }
 }
 
 // Tile t of a projection launch over rtn row tiles x nvt vocabulary tiles:
@@ -853,8 +825,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dw(const T* __restrict__ dz, int
 // Keys: (ordered_key(z) << 32) | (0xFFFFFFFF - id) -- a larger key is a larger
 // logit, or the same logit with a lower id; keys of one row are distinct.
 //
-// Pass 1 records, per row and tile, each lane's largest key (16 lanes per
-// row, each over 24 of the tile's columns): kTopkLanes x nvt sampled maxima.
+// Pass 1 records, per row and tile, 16 sampled maxima, each the largest key
+// of 24 of the tile's columns (each of the 8 lanes holding 48 columns of the
+// row gives two): kTopkLanes x nvt sampled maxima.
 // Threshold per row: the K-th largest of them.  They are keys of K distinct
 // logits of the row, so at least K logits are at or above it: every logit of
 // the top K is.  Rows with fewer than K sampled maxima take threshold 0 (every
@@ -928,18 +901,21 @@ __global__ __launch_bounds__(256) void k_topk_threshold(const uint32_t* __restri
   }
 }
 
-// Projection tile as in the forward.  PASS 0: the epilogue writes each lane's
-// largest key (padding columns excluded) to lmax.  PASS 1: it appends every
-// logit whose key is at or above its row's threshold to the row's candidate
-// list (one atomic add per row and tile with candidates; a list longer than
-// kTopkCap keeps kTopkCap entries and the select pass reports the row).
+// Projection tile as in the forward (transposed in the accumulators: each
+// lane holds 4 rows x 48 columns).  PASS 0: per row, the lane writes the
+// largest key of each half of its columns (padding columns excluded) to lmax.
+// PASS 1: it appends every logit of its columns whose key is at or above its
+// row's threshold to the row's candidate list (one atomic add per lane and
+// row with candidates; a list longer than kTopkCap keeps kTopkCap entries and
+// the select pass reports the row).
 template <typename T, int PASS>
 __global__ __launch_bounds__(512, 1) void k_topk_pass(const T* __restrict__ hk, int ldk, const T* __restrict__ W, int rows,
                                                       int d, int v, int nvt, uint32_t* __restrict__ lmax,
                                                       const uint32_t* __restrict__ thr, int* __restrict__ cnt,
                                                       uint64_t* __restrict__ cand) {
-  using G = ProjGemmT<T>;  // H_c through its k-tiled copy
-  __shared__ __attribute__((aligned(16))) char smem[proj_smem_bytes<G>()];
+  using G = ProjGemmX<T>;  // H_c through its k-tiled copy, tile transposed in the accumulators
+  static_assert(G::WAVES_COLS * 2 * 2 == kTopkLanes && G::FN * 4 == 12, "two maxima per lane and row");
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
   __shared__ uint32_t s_thr[G::BM];
   const int rtn = (rows + G::BM - 1) / G::BM;
   const int t = xcd_tile(blockIdx.x, rtn * nvt);
@@ -955,67 +931,62 @@ __global__ __launch_bounds__(512, 1) void k_topk_pass(const T* __restrict__ hk, 
   f32x16 acc[G::FM][G::FN];
   const Operand<T> A{hk, ldk, static_cast<long>((d + G::BK - 1) / G::BK) * ldk * G::BK, rt * G::BM, rows, d};
   const Operand<T> B{W, d, static_cast<long>(v) * d, vt * G::BN, v, d};
-  G::run(A, B, 0, d, smem, acc);
+  G::run(A, B, 0, d, smem, acc);  // ends with a barrier: s_thr is visible
 
-  float* stage = reinterpret_cast<float*>(smem);
+  const int lane = tid & 63, wave = tid >> 6, wm = wave / G::WAVES_COLS, wn = wave % G::WAVES_COLS;
+  const int half = lane >> 5;
+  const int c0 = wn * G::WN + 4 * half;  // column in tile of element 4 g + e of atom j: c0 + 32 j + 8 g + e
+  const int r0 = wm * G::WM + (lane & 31);
   const int ncols = min(G::BN, v - vt * G::BN);
-  const int g16 = tid >> 4, l16 = tid & 15;
 #pragma unroll
-  for (int h = 0; h < G::BM / kStageRows; ++h) {
-    stage_slice<G>(stage, acc, h);
-    lds_barrier();
-    for (int rr = g16; rr < kStageRows; rr += G::NT / 16) {
-      const int row = h * kStageRows + rr, grow = rt * G::BM + row;
-      if (grow >= rows) break;
-      const float* srow = stage + rr * kStagePitch + l16 * 4;
-      if (PASS == 0) {
-        uint32_t m = 0;
+  for (int i = 0; i < G::FM; ++i) {
+    const int row = r0 + 32 * i, grow = rt * G::BM + row;
+    if (grow >= rows) continue;
+    if (PASS == 0) {
+      uint32_t m[2] = {0u, 0u};  // groups j * 4 + g below 6 / from 6: 24 columns each
 #pragma unroll
-        for (int j = 0; j < G::BN / 64; ++j) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(srow + j * 64);
+      for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (j * 64 + l16 * 4 + e < ncols) m = max(m, ordered_key(x[e]));
-        }
-        lmax[static_cast<long>(grow) * nvt * kTopkLanes + vt * kTopkLanes + l16] = m;  // 0: no column here
-        continue;
-      }
-      const uint32_t th = s_thr[row];
-      int nh = 0;
+            if (c0 + 32 * j + 8 * g + e < ncols) {
+              uint32_t& mm = m[(j * 4 + g) < 6 ? 0 : 1];
+              mm = max(mm, ordered_key(acc[i][j][4 * g + e]));
+            }
+      uint32_t* out = lmax + (static_cast<long>(grow) * nvt + vt) * kTopkLanes + (wn * 2 + half) * 2;
+      out[0] = m[0];  // 0: no column here
+      out[1] = m[1];
+      continue;
+    }
+    const uint32_t th = s_thr[row];
+    int nh = 0;
 #pragma unroll
-      for (int j = 0; j < G::BN / 64; ++j) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(srow + j * 64);
+    for (int j = 0; j < G::FN; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) nh += (j * 64 + l16 * 4 + e < ncols && ordered_key(x[e]) >= th) ? 1 : 0;
-      }
-      const int total = static_cast<int>(group16_sum(static_cast<float>(nh)));
-      if (total > 0) {  // rare: the row's top-K region
-        int incl = nh;
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const int y = __shfl_up(incl, o, 16);
-          if (l16 >= o) incl += y;
-        }
-        int base = 0;
-        if (l16 == 0) base = atomicAdd(cnt + grow, total);
-        base = __shfl(base, 0, 16) + incl - nh;
-        uint64_t* out = cand + static_cast<long>(grow) * kTopkCap;
-        for (int j = 0; j < G::BN / 64 && nh > 0; ++j) {
+        for (int e = 0; e < 4; ++e)
+          nh += (c0 + 32 * j + 8 * g + e < ncols && ordered_key(acc[i][j][4 * g + e]) >= th) ? 1 : 0;
+    if (nh > 0) {  // rare: the row's top-K region
+      int base = atomicAdd(cnt + grow, nh);
+      uint64_t* out = cand + static_cast<long>(grow) * kTopkCap;
+#pragma unroll
+      for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int col = j * 64 + l16 * 4 + e;
-            const uint32_t key = ordered_key(srow[j * 64 + e]);
+            const int col = c0 + 32 * j + 8 * g + e;
+            const uint32_t key = ordered_key(acc[i][j][4 * g + e]);
             if (col < ncols && key >= th) {
               if (base < kTopkCap)
                 out[base] = (static_cast<uint64_t>(key) << 32) |
                             static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(vt * G::BN + col));
               ++base;
-              --nh;
             }
           }
-        }
-      }
     }
-    lds_barrier();
   }
 }
 
@@ -1106,7 +1077,7 @@ void launch_prep(const ChunkArgs& a, hipStream_t s) {
 
 void launch_fwd_proj(const ChunkArgs& a, hipStream_t s) {
   const int rtn = (a.rows + kProjBM - 1) / kProjBM;
-  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
+  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemmX<uint16_t>::NT);
   if (a.x_bf16)
     k_fwd_proj<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.hk), a.ldk,
                                                 static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v,
@@ -1133,7 +1104,7 @@ void launch_zero_loss(float* loss, hipStream_t s) { k_zero_loss<<<dim3(1), dim3(
 
 void launch_bwd_dz(const ChunkArgs& a, const float* lse, const float* g, hipStream_t s) {
   const int rtn = (a.rows + kProjBM - 1) / kProjBM;
-  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
+  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemmX<uint16_t>::NT);
   if (a.x_bf16)
     k_bwd_dz<uint16_t><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.hk), a.ldk,
                                               static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
@@ -1175,7 +1146,7 @@ void launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s) {
 
 void launch_topk_maxima(const ChunkArgs& a, uint32_t* lmax, hipStream_t s) {
   const int rtn = (a.rows + kProjBM - 1) / kProjBM;
-  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
+  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemmX<uint16_t>::NT);
   if (a.x_bf16)
     k_topk_pass<uint16_t, 0><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.hk), a.ldk,
                                                     static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
@@ -1195,7 +1166,7 @@ void launch_topk_threshold(const ChunkArgs& a, const uint32_t* lmax, uint32_t* t
 
 void launch_topk_collect(const ChunkArgs& a, const uint32_t* thr, int* cnt, uint64_t* cand, hipStream_t s) {
   const int rtn = (a.rows + kProjBM - 1) / kProjBM;
-  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemm<uint16_t>::NT);
+  const dim3 grid(xcd_grid(rtn * a.nvt)), block(ProjGemmX<uint16_t>::NT);
   if (a.x_bf16)
     k_topk_pass<uint16_t, 1><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(a.hk), a.ldk,
                                                     static_cast<const uint16_t*>(a.W), a.rows, a.d, a.v, a.nvt,
