@@ -94,9 +94,12 @@ typedef struct kd_problem {
   int32_t dw_chunks; /* chunks the backward takes at once, 0..8 (0 = 1): it
                         runs each of its kernels once per group of that many
                         chunks (the workspace holds their dZ), so dW is read
-                        and written once per group instead of per chunk; the
-                        results do not change (dH is summed over the V slices
-                        of one chunk's split either way) */
+                        and written once per group instead of per chunk.
+                        loss, lse and dH do not change (dH is summed over the
+                        V slices of one chunk's split either way); dW only in
+                        the grouping of its fp32 additions, and not at all
+                        when chunk is a multiple of the k tile (32 rows for
+                        bf16, 16 for fp32) */
 } kd_problem;
 
 /* Bytes of workspace the fwd and bwd calls need for `prob`.  Depends on
