@@ -59,6 +59,9 @@ def parse():
                          "(default: profiles/kd_gemms_<workload>_traffic.txt)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip timing the single-call variant (kd_chunked_fwd_bwd)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time the vendor GEMM library (hipBLASLt through torch.mm) on the three GEMM "
+                         "shapes of one backward group, bf16 in and out, for comparison")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy (y = -x, fp32) of this many MiB before warm-up: "
                          "the known-size dispatch that scales the memory counters of a --pmc run")
@@ -221,6 +224,50 @@ def cpu_baseline(inp, rows_n):
                       f"incl. their dW contribution), {dt:.1f} s",
             # linear extrapolation (the oracle's cost is per position): not measured
             "extrapolated_full_n_s": round(wl.n * dt / rows.size, 1)}
+
+
+def vendor_gemm(torch, H, W, rows, kernels, reps=10):
+    """The vendor GEMM library (hipBLASLt, through torch.mm) on the GEMM shapes
+    of one backward group of `rows` rows, bf16 in and out, next to the fused
+    kernel that does the same contraction (per-launch averages of this run).
+    Plain products only: no logsumexp, exponentials or teacher terms in the
+    projection, bf16 outputs where the fused dH and dW keep fp32 (dW added
+    into the fp32 accumulator)."""
+    C, D, V = rows, H.shape[1], W.shape[0]
+    if C > H.shape[0]:
+        return None
+    Hc = H[:C]
+    g = torch.Generator(device="cuda").manual_seed(1)
+    dz = torch.randn(C, V, dtype=torch.bfloat16, device="cuda", generator=g).mul_(1e-5)
+    z = torch.empty(C, V, dtype=torch.bfloat16, device="cuda")
+    dh = torch.empty(C, D, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty(V, D, dtype=torch.bfloat16, device="cuda")
+    shapes = {
+        "projection Z = H_c W^T (NT)": ("bwd_dz", lambda: torch.mm(Hc, W.t(), out=z)),
+        "dH = dZ W (NN)": ("bwd_dh", lambda: torch.mm(dz, W, out=dh)),
+        "dW = dZ^T H_c (TN)": ("bwd_dw", lambda: torch.mm(dz.t(), Hc, out=dw)),
+    }
+    flop = 2.0 * C * D * V
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"library": "hipBLASLt via torch.mm", "rows": C, "reps": reps, "gemms": {}}
+    for name, (kind, f) in shapes.items():
+        f()
+        f()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        fused = kernels.get(kind, {}).get("avg_ms")
+        res["gemms"][name] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                              "pct_peak": round(100.0 * flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                              "fused_kernel": kind, "fused_ms": round(fused, 4) if fused else None}
+    del dz, z, dh, dw
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -478,6 +525,10 @@ def main():
             "kernels": {k: round(t / n, 4) for k, (t, n) in tk.items() if n}}
         del wst
 
+    vendor = None
+    if args.vendor_gemm and wl.x_dtype == "bf16":
+        vendor = vendor_gemm(torch, H, W, args.dw_chunks * chunk, kernels)
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] cpu oracle baseline on {args.cpu_rows} rows", file=sys.stderr, flush=True)
@@ -511,6 +562,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "variants": variants,
+        "vendor_gemm": vendor,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
