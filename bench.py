@@ -121,15 +121,21 @@ def parse_sclk(text):
 
 
 class ClockSampler:
-    """Samples the GPU's current shader clock (pp_dpm_sclk in sysfs) from a
-    background thread while the timed steps run.  At this load the chip is
-    power-limited, so the clock it sustains differs from box to box; the
-    sampled mean is reported next to the step time as context."""
+    """Samples the GPU's current shader clock (pp_dpm_sclk in sysfs), and,
+    where the card's hwmon entries exist, its board power (power1_input,
+    microwatts, against power1_cap) and junction temperature (the temp*_input
+    labelled "junction", millidegrees), from a background thread while the
+    timed steps run.  At this load the chip runs at its power cap, so the
+    clock it sustains differs from box to box; the sampled means are reported
+    next to the step time as context."""
 
     def __init__(self, period_s=0.025):
         self.path = self._find()
+        self.hwmon = self._find_hwmon(self.path)
         self.period_s = period_s
         self.samples = []
+        self.power = []
+        self.temp = []
         self._stop = None
         self._thread = None
 
@@ -139,8 +145,37 @@ class ClockSampler:
         cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
         return cards[0] if len(cards) == 1 else None  # several GPUs: which one is ours is not checked
 
+    @staticmethod
+    def _find_hwmon(sclk_path):
+        """(power1_input, power1_cap, junction temp*_input) of the card, or None."""
+        import glob
+        if not sclk_path:
+            return None
+        dev = os.path.dirname(sclk_path)
+        for h in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+            pw, cap = os.path.join(h, "power1_input"), os.path.join(h, "power1_cap")
+            temp = None
+            for lab in sorted(glob.glob(os.path.join(h, "temp*_label"))):
+                try:
+                    if open(lab).read().strip() == "junction":
+                        temp = lab[:-len("label")] + "input"
+                except OSError:
+                    pass
+            if os.path.exists(pw):
+                return pw, (cap if os.path.exists(cap) else None), temp
+        return None
+
+    @staticmethod
+    def _read_int(path):
+        try:
+            with open(path) as f:
+                return int(f.read().strip())
+        except (OSError, ValueError):
+            return None
+
     def _run(self):
-        while not self._stop.is_set():
+        # one sample before the first look at the stop flag, so every run has one
+        while True:
             try:
                 with open(self.path) as f:
                     mhz = parse_sclk(f.read())
@@ -148,7 +183,16 @@ class ClockSampler:
                     self.samples.append(mhz)
             except OSError:
                 return
-            self._stop.wait(self.period_s)
+            if self.hwmon:
+                w = self._read_int(self.hwmon[0])
+                if w is not None:
+                    self.power.append(w / 1e6)
+                if self.hwmon[2]:
+                    t = self._read_int(self.hwmon[2])
+                    if t is not None:
+                        self.temp.append(t / 1e3)
+            if self._stop.wait(self.period_s):
+                return
 
     def __enter__(self):
         import threading
@@ -169,6 +213,22 @@ class ClockSampler:
             return None
         return {"mean": round(sum(self.samples) / len(self.samples), 1), "min": min(self.samples),
                 "max": max(self.samples), "samples": len(self.samples), "source": self.path}
+
+    def power_summary(self):
+        """Board power (W) over the samples, with the card's power cap, or None."""
+        if not self.power:
+            return None
+        cap = self._read_int(self.hwmon[1]) if self.hwmon and self.hwmon[1] else None
+        return {"mean": round(sum(self.power) / len(self.power), 1), "min": round(min(self.power), 1),
+                "max": round(max(self.power), 1), "cap": round(cap / 1e6, 1) if cap else None,
+                "samples": len(self.power), "source": self.hwmon[0]}
+
+    def temp_summary(self):
+        """Junction temperature (degrees C) over the samples, or None."""
+        if not self.temp:
+            return None
+        return {"mean": round(sum(self.temp) / len(self.temp), 1), "max": round(max(self.temp), 1),
+                "samples": len(self.temp)}
 
 
 def read_clock(path, kernel):
@@ -349,6 +409,8 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
     sclk = clock.summary()
+    power = clock.power_summary()
+    junction = clock.temp_summary()
     ms = e0.elapsed_time(e1) / args.steps
     per_step = sorted([e0.elapsed_time(marks[0])] +
                       [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)])
@@ -556,6 +618,10 @@ def main():
         # step's rate against the peak at that clock
         "observed_sclk_mhz": sclk,
         "pct_peak_at_observed_clock": round(100.0 * tflops / (peak * sclk["mean"] / 2400.0), 2) if sclk else None,
+        # board power and junction temperature sampled over the same steps (null where the card's
+        # hwmon entries are missing): at this load the chip sits at its power cap
+        "observed_power_w": power,
+        "observed_junction_c": junction,
         "peak_gib": round(peak_gib, 3),
         "profiled_ms_per_step": round(profiled_ms, 4),
         "loss": loss_v,

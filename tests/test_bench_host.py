@@ -75,3 +75,30 @@ def test_sclk_parse():
     with bench.ClockSampler() as c:   # no GPU here: no sysfs entry, or an idle reading
         pass
     assert c.summary() is None or c.summary()["samples"] >= 1
+    assert c.power_summary() is None or c.power_summary()["samples"] >= 1
+    assert c.temp_summary() is None or c.temp_summary()["samples"] >= 1
+
+
+def test_hwmon_sampling(tmp_path):
+    # a card directory laid out as the amdgpu driver does: the sampler finds
+    # power1_input / power1_cap and the temperature labelled "junction"
+    dev = tmp_path / "card0" / "device"
+    h = dev / "hwmon" / "hwmon3"
+    h.mkdir(parents=True)
+    (dev / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 1734Mhz *\n2: 2400Mhz\n")
+    (h / "power1_input").write_text("1398000000\n")
+    (h / "power1_cap").write_text("1400000000\n")
+    (h / "temp1_label").write_text("edge\n")
+    (h / "temp1_input").write_text("40000\n")
+    (h / "temp2_label").write_text("junction\n")
+    (h / "temp2_input").write_text("81000\n")
+    c = bench.ClockSampler()
+    c.path = str(dev / "pp_dpm_sclk")
+    c.hwmon = c._find_hwmon(c.path)
+    assert c.hwmon == (str(h / "power1_input"), str(h / "power1_cap"), str(h / "temp2_input"))
+    with c:
+        pass
+    assert c.summary()["mean"] == 1734.0
+    p = c.power_summary()
+    assert p["mean"] == 1398.0 and p["cap"] == 1400.0
+    assert c.temp_summary()["mean"] == 81.0
