@@ -147,7 +147,15 @@ class ClockSampler:
 
     @staticmethod
     def _find_hwmon(sclk_path):
-        """(power1_input, power1_cap, junction temp*_input) of the card, or None."""
+        """(power1_input, power1_cap, junction temp*_input) of the card, or None
+        (also on any error: the sensors are context, never a reason to fail)."""
+        try:
+            return ClockSampler._find_hwmon_paths(sclk_path)
+        except Exception:
+            return None
+
+    @staticmethod
+    def _find_hwmon_paths(sclk_path):
         import glob
         if not sclk_path:
             return None
@@ -170,7 +178,7 @@ class ClockSampler:
         try:
             with open(path) as f:
                 return int(f.read().strip())
-        except (OSError, ValueError):
+        except (OSError, ValueError, UnicodeDecodeError):
             return None
 
     def _run(self):
